@@ -1,0 +1,310 @@
+"""Float64 CPU oracle for exact attention with a learned per-head sink.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers, tables or pre/post-processing).
+
+What it computes (all arithmetic IEEE float64; inputs are the exact values the
+GPU sees, i.e. bf16 or fp32 values upcast):
+
+* ``attention_fwd`` -- causal (bottom-right aligned) attention over a sliding
+  window, with GQA head sharing and an optional per-query-head sink logit that
+  sits in the softmax denominator with no value vector.  The sink is the
+  "virtual anchor" logit of the Flint model page (cf-1.com, section on why the
+  kernel had to change) and the window is the "most recent 513 tokens" rule of
+  the same section.  O and the natural-log LSE are the plain definition:
+
+      s_j   = scale * <q_i, k_j>            for visible keys j
+      M     = max(max_j s_j, sigma)
+      l     = sum_j exp(s_j - M) + exp(sigma - M)
+      O_i   = sum_j exp(s_j - M) v_j / l
+      LSE_i = M + ln l
+
+  The LSE includes the sink term, because after the "rebase" update the
+  running denominator holds the sink's exponential (cf-1.com, fix two).  The
+  sink is compared with the *scaled* scores without being scaled itself
+  (cf-1.com, fix two: the sink is multiplied by log2(e) only, the running
+  max by the softmax scale in log2 units).
+
+* ``split_ranges`` / ``decode_partials`` / ``combine`` -- split-KV decode:
+  each split yields a normalised partial output and its (sink-free) LSE; the
+  combine reduces only the splits that exist, in their natural order, and adds
+  the sink exactly once as one more logit (FlashMLA patch stack page, section
+  3 "exact small-split combine").
+
+* ``naive_sink_row_sum_f32`` / ``rebase_sink_f32`` -- the two sink updates of
+  the cf-1.com page (fix two), evaluated in float32 so that tests can show the
+  old additive form overflowing and the rebased form staying finite.
+
+Readings of the pages where they are silent (each is listed in the design doc):
+window W keeps keys with p - W < j <= p (W <= 0: no window); query row i of
+Lq sits at absolute position p = i + Lk - Lq; the sink is per query head;
+max_offset = 0 and v_descale = 1.
+
+Parity pins: every public function here is pinned by tests/test_oracle.py
+against brute force, torch's float64 CPU attention, closed forms and exact
+integer counts.  Nothing is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LOG2E = 1.4426950408889634  # log2(e)
+
+
+# ---------------------------------------------------------------------------
+# index helpers (kept as small functions so that tests can plant mistakes)
+# ---------------------------------------------------------------------------
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head h: G = Hq/Hkv consecutive query heads share one.
+
+    GQA grouping as in the flash-attention repository profile (section 1,
+    "capabilities": MQA/GQA) -- consecutive query heads form a group.
+    """
+    G = Hq // Hkv
+    return h // G
+
+
+def query_position(i: int, Lq: int, Lk: int) -> int:
+    """Absolute position of query row i: the Lq queries are the last Lq positions."""
+    return i + Lk - Lq
+
+
+def visible_range(p: int, Lk: int, window: int) -> tuple[int, int]:
+    """Half-open key range [lo, hi) that the query at absolute position p sees.
+
+    Causal: keys j <= p.  Sliding window of W tokens including the query
+    itself: j > p - W.  W <= 0 means no window.  Keys beyond Lk do not exist.
+    """
+    hi = min(p + 1, Lk)
+    lo = 0 if window <= 0 else max(0, p - window + 1)
+    return lo, max(lo, hi)
+
+
+def effective_scale(scale: float) -> float:
+    """The softmax scale as the library receives it: a float32, upcast."""
+    return float(np.float32(scale))
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def _finish(scores: np.ndarray, vals: np.ndarray, sigma: float):
+    """O and LSE of one block of query rows from their scores (-inf = masked).
+
+    scores: [R, N] float64; vals: [N, D] float64; sigma: sink logit or -inf.
+    """
+    R = scores.shape[0]
+    D = vals.shape[1]
+    row_max = scores.max(axis=1) if scores.shape[1] else np.full(R, -np.inf)
+    M = np.maximum(row_max, sigma)
+    out = np.zeros((R, D))
+    lse = np.full(R, -np.inf)
+    ok = np.isfinite(M)  # rows that see at least one key or have a sink
+    if ok.any():
+        e = np.exp(scores[ok] - M[ok, None])           # masked entries -> 0
+        den = e.sum(axis=1) + np.exp(sigma - M[ok])
+        out[ok] = (e @ vals) / den[:, None]
+        lse[ok] = M[ok] + np.log(den)
+    return out, lse
+
+
+def attention_rows(q, k, v, sinks, b: int, h: int, rows, window: int, scale: float):
+    """O[b,h,rows,:] and LSE[b,h,rows] of the definition, for selected query rows.
+
+    q: [B,Hq,Lq,D], k/v: [B,Hkv,Lk,D] (any real dtype; upcast to float64),
+    sinks: [Hq] or None.  rows: iterable of query indices.
+    """
+    Hq, Lq = q.shape[1], q.shape[2]
+    Hkv, Lk = k.shape[1], k.shape[2]
+    kvh = kv_head_of(h, Hq, Hkv)
+    sc = effective_scale(scale)
+    sigma = -np.inf if sinks is None else float(np.float64(sinks[h]))
+    rows = np.asarray(list(rows), dtype=np.int64)
+    ranges = [visible_range(query_position(int(i), Lq, Lk), Lk, window) for i in rows]
+    lo = min((r[0] for r in ranges), default=0)
+    hi = max((r[1] for r in ranges), default=0)
+    hi = max(hi, lo)
+    Kb = np.asarray(k[b, kvh, lo:hi], dtype=np.float64)
+    Vb = np.asarray(v[b, kvh, lo:hi], dtype=np.float64)
+    Qb = np.asarray(q[b, h, rows], dtype=np.float64)
+    scores = sc * (Qb @ Kb.T)
+    cols = np.arange(lo, hi)
+    for r, (a, z) in enumerate(ranges):
+        scores[r, (cols < a) | (cols >= z)] = -np.inf
+    return _finish(scores, Vb, sigma)
+
+
+def attention_fwd(q, k, v, sinks, window: int, scale: float, block: int = 256):
+    """Full O [B,Hq,Lq,D] and LSE [B,Hq,Lq] of the definition (float64).
+
+    Query rows are evaluated ``block`` at a time purely to bound memory; each
+    row's arithmetic is the definition above.
+    """
+    B, Hq, Lq, D = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    out = np.zeros((B, Hq, Lq, D))
+    lse = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            for r0 in range(0, Lq, block):
+                rows = range(r0, min(Lq, r0 + block))
+                o, l = attention_rows(q, k, v, sinks, b, h, rows, window, scale)
+                out[b, h, r0:r0 + len(rows)] = o
+                lse[b, h, r0:r0 + len(rows)] = l
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# split-KV decode and combine
+# ---------------------------------------------------------------------------
+
+SPLIT_ALIGN = 64   # split boundaries fall on multiples of 64 keys from the window start
+MAX_SPLITS = 64
+
+
+def split_ranges(Lk: int, num_splits: int, window: int) -> list[tuple[int, int]]:
+    """The non-empty key ranges of the splits of one decode sequence.
+
+    The single query sits at position Lk - 1, so it sees [lo, Lk) with
+    lo = max(0, Lk - W) (no window: lo = 0).  The visible length n is cut into
+    chunks of ceil(n / num_splits) keys rounded up to a multiple of 64; only
+    the ceil(n / chunk) chunks that hold keys exist ("valid" splits).  Splits
+    whose range would be empty are not listed: they are never computed or
+    read (FlashMLA patch stack page, section 3).
+    """
+    ns = min(max(int(num_splits), 1), MAX_SPLITS)
+    Lk = max(int(Lk), 0)
+    lo = 0 if window <= 0 else max(0, Lk - window)
+    n = Lk - lo
+    if n <= 0:
+        return []
+    per = -(-n // ns)
+    chunk = -(-per // SPLIT_ALIGN) * SPLIT_ALIGN
+    out = []
+    s0 = lo
+    while s0 < Lk:
+        out.append((s0, min(s0 + chunk, Lk)))
+        s0 += chunk
+    return out
+
+
+def decode_partials(q, k_cache, v_cache, seqlens, num_splits, window: int, scale: float,
+                    max_splits: int = MAX_SPLITS):
+    """Per-split normalised outputs and sink-free LSEs of a decode step.
+
+    q: [B,Hq,1,D]; caches [B,Hkv,Lk_max,D]; seqlens, num_splits: [B] ints.
+    Returns o_part [B,Hq,max_splits,D], lse_part [B,Hq,max_splits] (lanes of
+    splits that do not exist hold NaN: nothing may read them), n_valid [B].
+
+    For split s with key set J_s:  lse_s = ln sum_{J_s} e^{s_j},
+    O_s = sum_{J_s} e^{s_j - lse_s} v_j  -- i.e. attention over J_s, no sink.
+    """
+    B, Hq, _, D = q.shape
+    o_part = np.full((B, Hq, max_splits, D), np.nan)
+    lse_part = np.full((B, Hq, max_splits), np.nan)
+    n_valid = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        Lk = int(seqlens[b])
+        sp = split_ranges(Lk, int(num_splits[b]), window)
+        n_valid[b] = len(sp)
+        for s, (a, z) in enumerate(sp):
+            kk = k_cache[b:b + 1, :, a:z]
+            vv = v_cache[b:b + 1, :, a:z]
+            for h in range(Hq):
+                # the query (position Lk-1) sees every key of [a, z): no window
+                # or causal limit cuts inside a split.
+                o, l = attention_rows(q[b:b + 1], kk, vv, None, 0, h, [0],
+                                      window=0, scale=scale)
+                o_part[b, h, s] = o[0]
+                lse_part[b, h, s] = l[0]
+    return o_part, lse_part, n_valid
+
+
+def combine(o_part, lse_part, n_valid, sinks):
+    """Merge the valid split partials of each (b, h) and add the sink once.
+
+    M = max(max_s lse_s, sigma); w_s = e^{lse_s - M};
+    den = sum_s w_s + e^{sigma - M}; O = sum_s w_s O_s / den; LSE = M + ln den.
+    Only lanes s < n_valid[b] are read, in order s = 0, 1, ...
+    """
+    B, Hq, _, D = o_part.shape
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(n_valid[b])
+        for h in range(Hq):
+            sigma = -np.inf if sinks is None else float(np.float64(sinks[h]))
+            ls = np.asarray(lse_part[b, h, :n], dtype=np.float64)
+            M = max(ls.max() if n else -np.inf, sigma)
+            if not np.isfinite(M):
+                continue
+            w = np.exp(ls - M)
+            den = w.sum() + math.exp(sigma - M) if np.isfinite(sigma) else w.sum()
+            acc = np.zeros(D)
+            for s in range(n):
+                acc += w[s] * np.asarray(o_part[b, h, s], dtype=np.float64)
+            out[b, h] = acc / den
+            lse[b, h] = M + math.log(den)
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, seqlens, sinks, window: int, scale: float):
+    """Unsplit decode: attention of each sequence's single query over its cache.
+
+    Equal by definition to ``attention_fwd`` with Lq = 1 on K[:, :, :Lk_b].
+    Returns O [B,Hq,D], LSE [B,Hq].
+    """
+    B, Hq, _, D = q.shape
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        Lk = int(seqlens[b])
+        kk = k_cache[b:b + 1, :, :Lk]
+        vv = v_cache[b:b + 1, :, :Lk]
+        for h in range(Hq):
+            o, l = attention_rows(q[b:b + 1], kk, vv, sinks, 0, h, [0], window, scale)
+            out[b, h] = o[0]
+            lse[b, h] = l[0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# the two sink updates of the cf-1.com page (fix two), in float32
+# ---------------------------------------------------------------------------
+
+def naive_sink_row_sum_f32(row_max, row_sum, sink, scale_log2):
+    """The old additive update: row_sum + 2^(sink*log2e - row_max*scale_log2).
+
+    row_max is in raw-score units, scale_log2 = scale * log2(e); max_offset = 0.
+    Evaluated in float32, as the kernel did.
+    """
+    f = np.float32
+    with np.errstate(over="ignore"):
+        t = f(f(sink) * f(LOG2E)) - f(f(row_max) * f(scale_log2))
+        return f(row_sum) + np.exp2(f(t), dtype=np.float32)
+
+
+def rebase_sink_f32(row_max, row_sum, sink, scale_log2):
+    """The rebased update, float32: returns (new row_max, new row_sum, sink_rescale).
+
+    old = row_max*scale_log2; new = max(old, sink*log2e);
+    sink_rescale = 2^(old - new); row_sum = row_sum*sink_rescale + 2^(sink*log2e - new);
+    row_max = new / scale_log2.  The output scale is sink_rescale / row_sum
+    (v_descale = 1).  Every exponent is <= 0, so no term exceeds 1.
+    """
+    f = np.float32
+    old = f(f(row_max) * f(scale_log2))
+    sl = f(f(sink) * f(LOG2E))
+    new = max(old, sl)
+    rescale = np.exp2(f(old - new), dtype=np.float32)
+    rs = f(f(row_sum) * rescale + np.exp2(f(sl - new), dtype=np.float32))
+    return f(new / f(scale_log2)), rs, rescale

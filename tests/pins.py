@@ -1,0 +1,176 @@
+"""Independent checks that pin the float64 oracle (used by test_oracle.py).
+
+Each function returns the largest discrepancy between the oracle and
+something the pages or mathematics fix on their own: brute-force softmax with
+plain Python loops, torch's float64 CPU attention (a library routine), closed
+forms of the sink, exact visible-key counts, and split/merge identities.  They
+are kept apart from the tests so that a test can plant a mistake in the oracle
+and show that some pin catches it.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def brute_force(q, k, v, sinks, window, scale):
+    """O, LSE by Python loops: softmax over the visible keys plus one extra
+    key whose logit is the sink and whose value vector is zero."""
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    sc = float(np.float32(scale))
+    O = np.zeros((B, Hq, Lq, D))
+    LSE = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i in range(Lq):
+                pos = Lk - Lq + i
+                logits, vals = [], []
+                for j in range(Lk):
+                    if j > pos:
+                        continue
+                    if window > 0 and pos - j >= window:
+                        continue
+                    logits.append(sc * math.fsum(q[b, h, i, d] * k[b, g, j, d] for d in range(D)))
+                    vals.append([v[b, g, j, d] for d in range(D)])
+                if sinks is not None:
+                    logits.append(float(sinks[h]))
+                    vals.append([0.0] * D)
+                if not logits:
+                    LSE[b, h, i] = -math.inf
+                    continue
+                top = max(logits)
+                ws = [math.exp(x - top) for x in logits]
+                tot = math.fsum(ws)
+                for d in range(D):
+                    O[b, h, i, d] = math.fsum(w * val[d] for w, val in zip(ws, vals)) / tot
+                LSE[b, h, i] = top + math.log(tot)
+    return O, LSE
+
+
+def torch_reference(q, k, v, sinks, window, scale):
+    """O, LSE from torch's float64 CPU flash attention (returns the logsumexp).
+
+    GQA by repeat_interleave of K/V along heads; causal + window as an additive
+    -inf mask built from index comparisons; the sink as one extra key of zero
+    vectors whose mask entry is the sink logit.
+    """
+    q_t = torch.from_numpy(np.asarray(q, dtype=np.float64))
+    k_t = torch.from_numpy(np.asarray(k, dtype=np.float64))
+    v_t = torch.from_numpy(np.asarray(v, dtype=np.float64))
+    B, Hq, Lq, D = q_t.shape
+    Hkv, Lk = k_t.shape[1], k_t.shape[2]
+    G = Hq // Hkv
+    k_t = k_t.repeat_interleave(G, dim=1)
+    v_t = v_t.repeat_interleave(G, dim=1)
+    pos = torch.arange(Lq).unsqueeze(1) + (Lk - Lq)
+    key = torch.arange(Lk).unsqueeze(0)
+    keep = key <= pos
+    if window > 0:
+        keep &= key > pos - window
+    mask = torch.zeros(Lq, Lk, dtype=torch.float64).masked_fill(~keep, -math.inf)
+    mask = mask.expand(B, Hq, Lq, Lk)
+    if sinks is not None:
+        k_t = torch.cat([k_t, torch.zeros(B, Hq, 1, D, dtype=torch.float64)], dim=2)
+        v_t = torch.cat([v_t, torch.zeros(B, Hq, 1, D, dtype=torch.float64)], dim=2)
+        col = torch.from_numpy(np.asarray(sinks, dtype=np.float64)).view(1, Hq, 1, 1)
+        mask = torch.cat([mask, col.expand(B, Hq, Lq, 1)], dim=3)
+    sc = float(np.float32(scale))
+    o, lse = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(
+        q_t, k_t, v_t, 0.0, False, attn_mask=mask.contiguous(), scale=sc)
+    return o.numpy(), lse.numpy()
+
+
+def err_vs_brute(seed=0, B=2, Hq=4, Hkv=2, Lq=6, Lk=8, D=3, window=3, sink_scale=1.0,
+                 with_sink=True):
+    q, k, v = rand((B, Hq, Lq, D), seed), rand((B, Hkv, Lk, D), seed + 1), rand((B, Hkv, Lk, D), seed + 2)
+    sinks = rand(Hq, seed + 3, sink_scale) if with_sink else None
+    scale = 0.7
+    o, l = oracle.attention_fwd(q, k, v, sinks, window, scale)
+    ob, lb = brute_force(q, k, v, sinks, window, scale)
+    return max(np.abs(o - ob).max(), np.abs(l - lb).max())
+
+
+def err_vs_torch(seed=0, B=1, Hq=4, Hkv=2, Lq=100, Lk=130, D=16, window=7, with_sink=True):
+    q, k, v = rand((B, Hq, Lq, D), seed), rand((B, Hkv, Lk, D), seed + 1), rand((B, Hkv, Lk, D), seed + 2)
+    sinks = rand(Hq, seed + 3, 2.0) if with_sink else None
+    scale = 1 / math.sqrt(D)
+    o, l = oracle.attention_fwd(q, k, v, sinks, window, scale, block=37)
+    ot, lt = torch_reference(q, k, v, sinks, window, scale)
+    return max(np.abs(o - ot).max(), np.abs(l - lt).max())
+
+
+def visible_count(i, Lq, Lk, window):
+    """Number of keys the query row i sees, by counting integers."""
+    p = i + Lk - Lq
+    n = 0
+    for j in range(Lk):
+        if j <= p and (window <= 0 or p - j < window):
+            n += 1
+    return n
+
+
+def err_counts(Lq=40, Lk=50, window=7, sink=None, D=2):
+    """Q = 0 makes every score 0; V = 1 then gives O = n/(n + e^sigma) and
+    LSE = ln(n + e^sigma) with n the exact visible-key count."""
+    q = np.zeros((1, 1, Lq, D))
+    k = rand((1, 1, Lk, D), 5)
+    v = np.ones((1, 1, Lk, D))
+    sinks = None if sink is None else np.array([sink])
+    o, l = oracle.attention_fwd(q, k, v, sinks, window, 0.3)
+    n = np.array([visible_count(i, Lq, Lk, window) for i in range(Lq)], dtype=np.float64)
+    es = 0.0 if sink is None else math.exp(sink)
+    want_o = n / (n + es)
+    want_l = np.log(n + es)
+    return max(np.abs(o[0, 0, :, 0] - want_o).max(), np.abs(l[0, 0] - want_l).max())
+
+
+def err_sink_closed_form(seed=0, sigma=2.5, window=9, Lq=30, Lk=30, D=8):
+    """Adding a sink sigma multiplies O by sigmoid(LSE0 - sigma) and turns
+    LSE0 into logaddexp(LSE0, sigma), where 0 marks the sink-free result."""
+    q, k, v = rand((1, 2, Lq, D), seed), rand((1, 1, Lk, D), seed + 1), rand((1, 1, Lk, D), seed + 2)
+    o0, l0 = oracle.attention_fwd(q, k, v, None, window, 0.4)
+    o1, l1 = oracle.attention_fwd(q, k, v, np.array([sigma, sigma]), window, 0.4)
+    sig = 1.0 / (1.0 + np.exp(sigma - l0))
+    return max(np.abs(o1 - o0 * sig[..., None]).max(), np.abs(l1 - np.logaddexp(l0, sigma)).max())
+
+
+def err_gqa(seed=0, Hq=8, Hkv=2, L=40, D=8, window=11):
+    """GQA equals MHA on K/V whose heads are repeated G times (consecutive)."""
+    q, k, v = rand((2, Hq, L, D), seed), rand((2, Hkv, L, D), seed + 1), rand((2, Hkv, L, D), seed + 2)
+    sinks = rand(Hq, seed + 3)
+    o, l = oracle.attention_fwd(q, k, v, sinks, window, 0.5)
+    G = Hq // Hkv
+    o2, l2 = oracle.attention_fwd(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), sinks, window, 0.5)
+    return max(np.abs(o - o2).max(), np.abs(l - l2).max())
+
+
+def err_split_combine(Lks=(1, 2, 63, 64, 65, 127, 129, 700, 1025), windows=(0, 513, 64, 1),
+                      splits=(1, 2, 3, 7, 31, 32, 33, 63, 64), Hq=4, Hkv=2, D=8, seed=0):
+    """Split-KV partials merged by the combine equal the unsplit decode."""
+    Lmax = max(Lks)
+    B = len(Lks)
+    q = rand((B, Hq, 1, D), seed)
+    kc, vc = rand((B, Hkv, Lmax, D), seed + 1), rand((B, Hkv, Lmax, D), seed + 2)
+    sinks = rand(Hq, seed + 3)
+    seqlens = np.array(Lks)
+    worst = 0.0
+    for W in windows:
+        ref_o, ref_l = oracle.decode(q, kc, vc, seqlens, sinks, W, 0.35)
+        for ns in splits:
+            nsv = np.full(B, ns)
+            op, lp, nv = oracle.decode_partials(q, kc, vc, seqlens, nsv, W, 0.35)
+            o, l = oracle.combine(op, lp, nv, sinks)
+            worst = max(worst, np.abs(o - ref_o).max(), np.abs(l - ref_l).max())
+    return worst

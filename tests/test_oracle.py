@@ -1,0 +1,334 @@
+"""Pins of the float64 oracle (CPU only).
+
+Every function of oracle/attention.py is checked here against something other
+than itself: brute force, a library routine, closed forms, exact counts or
+split/merge identities.  The last tests plant mistakes in the oracle and show
+that a pin catches each one.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oa
+import pins
+
+TOL = 1e-12
+
+
+# --- forward ----------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [0, 1, 2, 3, 5, 100])
+@pytest.mark.parametrize("heads", [(1, 1), (2, 1), (4, 2), (3, 3)])
+def test_brute_force_small(window, heads):
+    Hq, Hkv = heads
+    for seed, (Lq, Lk) in enumerate([(6, 8), (8, 8), (1, 5), (3, 3)]):
+        assert pins.err_vs_brute(seed=seed, Hq=Hq, Hkv=Hkv, Lq=Lq, Lk=Lk, window=window) < TOL
+        assert pins.err_vs_brute(seed=seed, Hq=Hq, Hkv=Hkv, Lq=Lq, Lk=Lk, window=window,
+                                 with_sink=False) < TOL
+
+
+def test_brute_force_extreme_sinks():
+    for s in (30.0, 100.0):
+        assert pins.err_vs_brute(seed=7, sink_scale=s) < TOL
+
+
+@pytest.mark.parametrize("window", [0, 1, 7, 64, 129, 513])
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_torch_flash_cpu(window, with_sink):
+    assert pins.err_vs_torch(window=window, with_sink=with_sink) < 1e-12
+    assert pins.err_vs_torch(seed=3, Hq=2, Hkv=2, Lq=77, Lk=77, window=window,
+                             with_sink=with_sink) < 1e-12
+
+
+@pytest.mark.parametrize("window", [1, 2, 7, 512, 513, 514, 50, 0])
+@pytest.mark.parametrize("sink", [None, -3.0, 0.0, 2.0])
+def test_exact_counts(window, sink):
+    assert pins.err_counts(Lq=40, Lk=50, window=window, sink=sink) < TOL
+    assert pins.err_counts(Lq=600, Lk=600, window=window, sink=sink) < TOL
+
+
+def test_counts_no_sink_give_integers():
+    q = np.zeros((1, 1, 700, 4))
+    k = pins.rand((1, 1, 700, 4), 1)
+    v = pins.rand((1, 1, 700, 4), 2)
+    _, lse = oracle.attention_fwd(q, k, v, None, 513, 0.1)
+    n = np.exp(lse[0, 0])
+    assert np.allclose(n, np.minimum(np.arange(700) + 1, 513), rtol=0, atol=1e-9)
+
+
+def test_window_at_least_length_is_full_causal():
+    q, k, v = pins.rand((1, 2, 256, 8), 1), pins.rand((1, 1, 256, 8), 2), pins.rand((1, 1, 256, 8), 3)
+    s = np.array([0.3, 100.0])
+    a = oracle.attention_fwd(q, k, v, s, 513, 0.125)
+    b = oracle.attention_fwd(q, k, v, s, 0, 0.125)
+    c = oracle.attention_fwd(q, k, v, s, 256, 0.125)
+    for x, y in ((a, b), (a, c)):
+        assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+
+
+def test_window_one_is_sigmoid_of_self_score():
+    D = 8
+    q, k, v = pins.rand((1, 1, 20, D), 1), pins.rand((1, 1, 20, D), 2), pins.rand((1, 1, 20, D), 3)
+    sigma, scale = 0.4, 0.3
+    o, l = oracle.attention_fwd(q, k, v, np.array([sigma]), 1, scale)
+    sc = float(np.float32(scale))
+    s_ii = sc * np.einsum("id,id->i", q[0, 0], k[0, 0])
+    want = v[0, 0] / (1.0 + np.exp(sigma - s_ii))[:, None]
+    assert np.abs(o[0, 0] - want).max() < TOL
+    assert np.abs(l[0, 0] - np.logaddexp(s_ii, sigma)).max() < TOL
+
+
+@pytest.mark.parametrize("sigma", [-30.0, -1.0, 0.0, 2.5, 20.0, 100.0])
+def test_sink_closed_form(sigma):
+    assert pins.err_sink_closed_form(sigma=sigma) < TOL
+
+
+def test_sink_to_minus_infinity_is_plain_attention():
+    q, k, v = pins.rand((1, 2, 30, 8), 1), pins.rand((1, 1, 30, 8), 2), pins.rand((1, 1, 30, 8), 3)
+    a = oracle.attention_fwd(q, k, v, None, 9, 0.4)
+    b = oracle.attention_fwd(q, k, v, np.array([-np.inf, -np.inf]), 9, 0.4)
+    c = oracle.attention_fwd(q, k, v, np.array([-800.0, -800.0]), 9, 0.4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.abs(a[0] - c[0]).max() == 0.0
+
+
+def test_sink_dominance():
+    q, k, v = pins.rand((1, 1, 64, 16), 1), pins.rand((1, 1, 64, 16), 2), pins.rand((1, 1, 64, 16), 3)
+    o, l = oracle.attention_fwd(q, k, v, np.array([100.0]), 0, 0.25)
+    assert np.isfinite(o).all() and np.abs(o).max() < 1e-30
+    assert np.abs(l - 100.0).max() < 1e-30
+    for sigma in (20.0, 30.0):
+        o, l = oracle.attention_fwd(q, k, v, np.array([sigma]), 0, 0.25)
+        sc = 0.25 * np.einsum("id,jd->ij", q[0, 0], k[0, 0])
+        smax = sc.max()
+        n = np.arange(64) + 1
+        bound = n * np.exp(smax - sigma) * np.abs(v).max()
+        assert (np.abs(o[0, 0]).max(axis=1) <= bound).all()
+        assert (l[0, 0] >= sigma).all() and (l[0, 0] - sigma < n * np.exp(smax - sigma)).all()
+
+
+def test_gqa_is_repeated_mha():
+    assert pins.err_gqa() < TOL
+    assert pins.err_gqa(Hq=8, Hkv=8) < TOL
+    assert pins.err_gqa(Hq=8, Hkv=1) < TOL
+
+
+def test_empty_rows():
+    # Lk = 0: no key is visible; O = 0 and LSE = sink (or -inf without one).
+    q = pins.rand((1, 2, 1, 4), 1)
+    k = np.zeros((1, 1, 0, 4))
+    o, l = oracle.attention_rows(q, k, k, np.array([1.5, -2.0]), 0, 0, [0], 0, 0.5)
+    assert np.array_equal(o, np.zeros((1, 4))) and l[0] == 1.5
+    o, l = oracle.attention_rows(q, k, k, None, 0, 1, [0], 0, 0.5)
+    assert np.array_equal(o, np.zeros((1, 4))) and l[0] == -np.inf
+
+
+def test_convex_combination_bounds():
+    q, k, v = pins.rand((1, 1, 90, 8), 1), pins.rand((1, 1, 90, 8), 2), pins.rand((1, 1, 90, 8), 3)
+    o, _ = oracle.attention_fwd(q, k, v, None, 20, 0.5)
+    for i in range(90):
+        lo = max(0, i - 19)
+        vis = v[0, 0, lo:i + 1]
+        assert (o[0, 0, i] <= vis.max(axis=0) + 1e-12).all()
+        assert (o[0, 0, i] >= vis.min(axis=0) - 1e-12).all()
+
+
+# --- split-KV decode ----------------------------------------------------------
+
+def test_split_ranges_partition():
+    for W in (0, 1, 64, 513, 1000):
+        for Lk in (0, 1, 2, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1025, 4097, 32768):
+            lo = 0 if W <= 0 else max(0, Lk - W)
+            for ns in range(1, 65):
+                sp = oracle.split_ranges(Lk, ns, W)
+                assert len(sp) <= ns
+                covered = [j for a, z in sp for j in range(a, z)]
+                assert covered == list(range(lo, Lk))
+                assert all(z > a for a, z in sp)
+                if sp:
+                    chunk = sp[0][1] - sp[0][0] if len(sp) > 1 else None
+                    if chunk is not None:
+                        assert chunk % 64 == 0
+                        assert all(z - a == chunk for a, z in sp[:-1])
+                        # the smallest multiple of 64 that lets ns chunks cover the range
+                        assert chunk == max(64, -(-(-(-(Lk - lo) // ns)) // 64) * 64)
+
+
+def test_split_ranges_examples():
+    # 1025 keys in 64 splits: chunks of 64, so 17 splits exist, the last holds one key.
+    sp = oracle.split_ranges(1025, 64, 0)
+    assert len(sp) == 17 and sp[-1] == (1024, 1025)
+    assert oracle.split_ranges(0, 5, 0) == []
+    assert oracle.split_ranges(32768, 64, 0) == [(512 * s, 512 * s + 512) for s in range(64)]
+    assert oracle.split_ranges(5000, 3, 513) == [(4487, 4679), (4679, 4871), (4871, 5000)]
+
+
+def test_split_combine_equals_unsplit():
+    assert pins.err_split_combine() < TOL
+
+
+def test_decode_equals_forward_with_one_query():
+    q = pins.rand((3, 4, 1, 8), 1)
+    kc, vc = pins.rand((3, 2, 300, 8), 2), pins.rand((3, 2, 300, 8), 3)
+    sinks = pins.rand(4, 4)
+    seqlens = np.array([300, 17, 129])
+    for W in (0, 5, 513):
+        o, l = oracle.decode(q, kc, vc, seqlens, sinks, W, 0.3)
+        for b in range(3):
+            L = seqlens[b]
+            of, lf = oracle.attention_fwd(q[b:b + 1], kc[b:b + 1, :, :L], vc[b:b + 1, :, :L], sinks, W, 0.3)
+            assert np.array_equal(o[b], of[0, :, 0]) and np.array_equal(l[b], lf[0, :, 0])
+
+
+def test_combine_reads_only_valid_lanes():
+    q = pins.rand((2, 2, 1, 8), 1)
+    kc, vc = pins.rand((2, 1, 200, 8), 2), pins.rand((2, 1, 200, 8), 3)
+    seqlens, ns = np.array([200, 70]), np.array([64, 64])
+    op, lp, nv = oracle.decode_partials(q, kc, vc, seqlens, ns, 0, 0.3)
+    assert list(nv) == [4, 2]
+    assert np.isnan(op[0, :, 4:]).all() and np.isnan(lp[1, :, 2:]).all()
+    o, l = oracle.combine(op, lp, nv, np.array([0.5, 9.0]))
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+def test_combine_one_split_is_the_sink_rebase():
+    # With one split the combine is the sink update of a single partial:
+    # O = O_0 * sigmoid(lse_0 - sigma), LSE = logaddexp(lse_0, sigma).
+    o_part = pins.rand((1, 1, 1, 8), 1)
+    lse_part = np.array([[[3.0]]])
+    for sigma in (-5.0, 3.0, 100.0):
+        o, l = oracle.combine(o_part, lse_part, np.array([1]), np.array([sigma]))
+        assert np.abs(o[0, 0] - o_part[0, 0, 0] / (1 + math.exp(sigma - 3.0))).max() < TOL
+        assert abs(l[0, 0] - np.logaddexp(3.0, sigma)) < TOL
+
+
+def test_combine_empty_sequence():
+    o, l = oracle.combine(np.zeros((1, 2, 4, 3)), np.zeros((1, 2, 4)), np.array([0]), np.array([0.7, 2.0]))
+    assert np.array_equal(o, np.zeros((1, 2, 3))) and list(l[0]) == [0.7, 2.0]
+    o, l = oracle.combine(np.zeros((1, 1, 4, 3)), np.zeros((1, 1, 4)), np.array([0]), None)
+    assert l[0, 0] == -np.inf and np.array_equal(o, np.zeros((1, 1, 3)))
+
+
+# --- the two sink updates of the Flint patch (float32) ---------------------
+
+def test_naive_sink_update_overflows_in_f32():
+    # Running max 3.0 in raw units, scale 1/8: content exponent ~0.54, while
+    # the sink +100 contributes 2^(144.27 - 0.54) -- beyond float32's range.
+    scale_log2 = np.float32(0.125 * oracle.LOG2E)
+    out = oracle.naive_sink_row_sum_f32(3.0, 5.0, 100.0, scale_log2)
+    assert np.isinf(out)
+    rm, rs, rescale = oracle.rebase_sink_f32(3.0, 5.0, 100.0, scale_log2)
+    assert np.isfinite(rs) and np.isfinite(rescale) and rs >= 1.0 and rescale <= 1.0
+
+
+@pytest.mark.parametrize("sink", [-40.0, -2.0, 0.0, 1.0, 20.0, 100.0])
+def test_rebase_update_matches_definition(sink):
+    # Online state of one row after all keys: row_max (raw units) and
+    # row_sum = sum 2^((x_j - row_max) * scale_log2); the rebase then gives
+    # LSE = ln2 * (new_max_log2 + log2 row_sum) and O = acc * rescale / row_sum.
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(40).astype(np.float32) * np.float32(8)     # raw q.k
+    vals = rng.standard_normal((40, 4))
+    scale = 0.125
+    sl2 = np.float32(scale * oracle.LOG2E)
+    row_max = np.float32(x.max())
+    p = np.exp2((x - row_max) * sl2, dtype=np.float32)
+    row_sum = np.float32(p.sum(dtype=np.float32))
+    acc = (p[:, None].astype(np.float64) * vals).sum(axis=0)
+    new_max, new_sum, rescale = oracle.rebase_sink_f32(row_max, row_sum, sink, sl2)
+    lse = math.log(2) * (float(new_max) * float(sl2) + math.log2(float(new_sum)))
+    o = acc * float(rescale) / float(new_sum)
+    s = scale * x.astype(np.float64)
+    want_l = np.logaddexp(np.logaddexp.reduce(s), sink)
+    w = np.exp(s - want_l)
+    want_o = (w[:, None] * vals).sum(axis=0)
+    assert abs(lse - want_l) < 1e-5 * max(1.0, abs(want_l))
+    assert np.abs(o - want_o).max() < 1e-5
+
+
+# --- stored regression fixture ----------------------------------------------
+
+def test_golden_fixture():
+    here = os.path.join(os.path.dirname(__file__), "golden", "oracle_small.json")
+    with open(here) as f:
+        g = json.load(f)
+    q, k, v = (np.array(g[n]) for n in ("q", "k", "v"))
+    o, l = oracle.attention_fwd(q, k, v, np.array(g["sinks"]), g["window"], g["scale"])
+    assert np.abs(o - np.array(g["out"])).max() < 1e-14
+    assert np.abs(l - np.array(g["lse"])).max() < 1e-14
+
+
+# --- planted mistakes: each must be caught by some pin ------------------------
+
+def _caught(monkeypatch, name, fake):
+    with monkeypatch.context() as m:
+        m.setattr(oa, name, fake)
+        errs = [
+            pins.err_vs_brute(window=3),
+            pins.err_vs_brute(window=0, Hq=4, Hkv=2, Lq=5, Lk=8),
+            pins.err_vs_torch(window=7),
+            pins.err_counts(window=7, sink=1.0),
+            pins.err_sink_closed_form(),
+            pins.err_gqa(),
+        ]
+    return max(errs) > 1e-6
+
+
+def test_pins_catch_window_off_by_one(monkeypatch):
+    def fake(p, Lk, window):
+        hi = min(p + 1, Lk)
+        lo = 0 if window <= 0 else max(0, p - window)   # one key too many
+        return lo, max(lo, hi)
+    assert _caught(monkeypatch, "visible_range", fake)
+
+
+def test_pins_catch_top_left_alignment(monkeypatch):
+    assert _caught(monkeypatch, "query_position", lambda i, Lq, Lk: i)
+
+
+def test_pins_catch_wrong_kv_head(monkeypatch):
+    assert _caught(monkeypatch, "kv_head_of", lambda h, Hq, Hkv: h % Hkv)
+
+
+def test_pins_catch_sink_dropped_from_lse(monkeypatch):
+    orig = oa._finish
+
+    def fake(scores, vals, sigma):
+        o, _ = orig(scores, vals, sigma)
+        _, l = orig(scores, vals, -np.inf)
+        return o, l
+    assert _caught(monkeypatch, "_finish", fake)
+
+
+def test_pins_catch_scaled_sink(monkeypatch):
+    orig = oa.attention_rows
+
+    def fake(q, k, v, sinks, b, h, rows, window, scale):
+        s = None if sinks is None else np.asarray(sinks, dtype=np.float64) * scale
+        return orig(q, k, v, s, b, h, rows, window, scale)
+    with monkeypatch.context() as m:
+        m.setattr(oa, "attention_rows", fake)
+        assert pins.err_vs_torch(window=7) > 1e-6
+
+
+def test_pins_catch_split_mistakes(monkeypatch):
+    orig = oa.split_ranges
+
+    def drop_last(Lk, ns, window):
+        return orig(Lk, ns, window)[:-1] if ns > 1 else orig(Lk, ns, window)
+    with monkeypatch.context() as m:
+        m.setattr(oa, "split_ranges", drop_last)
+        assert pins.err_split_combine(splits=(2, 7)) > 1e-6
+
+    def overlap(Lk, ns, window):
+        return [(max(0, a - 1), z) for a, z in orig(Lk, ns, window)]
+    with monkeypatch.context() as m:
+        m.setattr(oa, "split_ranges", overlap)
+        assert pins.err_split_combine(splits=(2, 7)) > 1e-6
