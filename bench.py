@@ -1,0 +1,230 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = the whole path on resident synthetic inputs:
+  attn_fwd            sliding-window prefill  B1 Hq64 Hkv8 L8192 D128 bf16, window 513,
+                      sinks (heads h%8==0 at +20), O written in bf16
+  attn_decode_splitkv split-KV decode  B64 Hq64 Hkv8 D128 bf16, Lk ~ U{1024..32768},
+                      num_splits = clamp(ceil(Lk/512), 1, 64)
+  attn_combine        merge of the valid splits, sink added once
+
+Prints one JSON line.  `value` is the prefill's TFLOP/s (algorithmic flops:
+4*D per unmasked pair) from HIP events around each attn_fwd launch on the
+stream it runs on; decode GB/s (algorithmic bytes: the K/V rows each query
+sees plus q, O and LSE) is reported beside it.  The float64 CPU oracle is
+timed on a bounded sample of the prefill on the host cores (rank 0 only).
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; stored traffic counters are used only if it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_attn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current sources, or None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def decode_bytes(seqlens, Hq, Hkv, D, window) -> int:
+    lk = np.asarray(seqlens, np.int64)
+    if window > 0:
+        lk = np.minimum(lk, window)
+    kv = int(lk.sum()) * Hkv * D * 2 * 2
+    B = len(seqlens)
+    return kv + B * Hq * D * 2 + B * Hq * D * 2 + B * Hq * 4 + Hq * 4
+
+
+def cpu_baseline(w, q, k, v, sinks, budget_s=20.0):
+    """Time the float64 oracle on whole heads of the prefill until ~budget_s of work."""
+    import oracle
+    from exact_attention_attn_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    G = w.Hq // w.Hkv
+    per_head = w.flops() // (w.B * w.Hq)
+    done, flops, t0 = 0, 0, time.perf_counter()
+    for h in range(w.Hq):
+        kvh = h // G
+        oracle.attention_fwd(W.as_float(q[:, h:h + 1], w.dtype), W.as_float(k[:, kvh:kvh + 1], w.dtype),
+                             W.as_float(v[:, kvh:kvh + 1], w.dtype), sinks[h:h + 1], w.window, w.scale)
+        done += 1
+        flops += per_head
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.Hq} heads of {w.name} (all rows), float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", default="swa_prefill",
+                    help="prefill workload (swa_prefill is the headline; others for study)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_attn_amd as A
+    from exact_attention_attn_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    A.load_library()
+    dev = torch.device("cuda", 0)
+
+    def up(x, dtype):
+        if dtype == W.BF16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    # prefill inputs
+    wp = W.WORKLOADS[args.prefill]
+    qh, kh, vh, sh = W.prefill_inputs(wp)
+    q, k, v = up(qh, wp.dtype), up(kh, wp.dtype), up(vh, wp.dtype)
+    s = torch.from_numpy(sh).to(dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    # decode inputs
+    wd = W.SPLITKV_DECODE
+    dq, dk, dv, seqlens, nsplits, dsinks = W.decode_inputs(wd)
+    qd, kd, vd = up(dq, W.BF16), up(dk, W.BF16), up(dv, W.BF16)
+    del dk, dv
+    sl = torch.from_numpy(seqlens).to(dev)
+    ns = torch.from_numpy(nsplits).to(dev)
+    ds = torch.from_numpy(dsinks).to(dev)
+    MS = 64
+    op = torch.empty((wd.B, wd.Hq, MS, wd.D), dtype=torch.float32, device=dev)
+    lp = torch.empty((wd.B, wd.Hq, MS), dtype=torch.float32, device=dev)
+    dout = torch.empty((wd.B, wd.Hq, 1, wd.D), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((wd.B, wd.Hq), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream(device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+          for _ in range(args.warmup + args.steps)]
+
+    def step(i):
+        e = ev[i]
+        e[0].record(stream)
+        A.attn_fwd(q, k, v, s, out, lse, window=wp.window, scale=wp.scale, stream=stream)
+        e[1].record(stream)
+        A.attn_decode_splitkv(qd, kd, vd, sl, ns, op, lp, window=wd.window, scale=wd.scale,
+                              stream=stream)
+        e[2].record(stream)
+        A.attn_combine(op, lp, sl, ns, ds, dout, dlse, Lk_max=wd.Lk_max, window=wd.window,
+                       stream=stream)
+        e[3].record(stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, args.warmup + args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+    timed = ev[args.warmup:]
+    t_fwd = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e-3
+    t_dec = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e-3
+    t_cmb = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e-3
+
+    flops = wp.flops()
+    tflops = flops / t_fwd.mean() / 1e12
+    dbytes = decode_bytes(seqlens, wd.Hq, wd.Hkv, wd.D, wd.window)
+    dec_gbps = dbytes / (t_dec.mean() + t_cmb.mean()) / 1e9
+    traffic = stored_traffic("fwd_bf16_kernel<128,false>:" + wp.name)
+
+    res = {
+        "metric": "attn fwd TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wp.name} B{wp.B} Hq{wp.Hq} Hkv{wp.Hkv} L{wp.L} D{wp.D} window{wp.window} "
+                        f"+ {wd.name} B{wd.B} Hq{wd.Hq} Hkv{wd.Hkv} D{wd.D} Lk<={wd.Lk_max}",
+            "prefill_flops": flops,
+            "decode_bytes": dbytes,
+            "decode_sum_Lk": int(np.asarray(seqlens, np.int64).sum()),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "fwd_bf16_kernel<128,false>",
+            "ms_per_launch": round(t_fwd.mean() * 1e3, 4),
+        },
+        "decode": {
+            "GB/s": round(dec_gbps, 1),
+            "frac_hbm": round(dec_gbps / PEAK_HBM_GBPS, 4),
+            "decode_ms": round(t_dec.mean() * 1e3, 4),
+            "combine_ms": round(t_cmb.mean() * 1e3, 4),
+            "decode_only_GB/s": round(dbytes / t_dec.mean() / 1e9, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wp, qh, kh, vh, sh)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

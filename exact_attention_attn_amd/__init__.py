@@ -1,0 +1,186 @@
+"""MI355X (gfx950) exact attention: thin Python binding over the C ABI in include/attn.h.
+
+The functions here only marshal torch tensors (device pointers, sizes, the
+current HIP stream) into the C calls of ``libattn_mi355x.so``; every step of
+the computation runs in the library's HIP kernels.  Importing this package
+does not load the library; the first call does, and fails loudly when it has
+not been built (``python -m exact_attention_attn_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["attn_fwd", "attn_decode_splitkv", "attn_combine", "attn_strerror", "AttnError",
+           "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
+
+ATTN_BF16 = 0
+ATTN_F32 = 1
+MAX_SPLITS = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn_mi355x.so"
+_lock = threading.Lock()
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+_SIGNATURES = {
+    "attn_fwd": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp],
+    "attn_decode_splitkv": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
+    "attn_combine": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "attn_strerror": [_i],
+    "attn_version": [],
+}
+
+
+class AttnError(RuntimeError):
+    """A non-zero return code of the C library."""
+
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn}: {attn_strerror(code)} (code {code})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built HIP library (raises if it is missing: there is no fallback)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build it with `python -m exact_attention_attn_amd.build`")
+            lib = ctypes.CDLL(path)
+            for name, args in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = ctypes.c_char_p if name in ("attn_strerror", "attn_version") else ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def attn_strerror(code: int) -> str:
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bfloat16 or float32")
+
+
+def _dev(t, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise AttnError(fn, rc)
+
+
+def attn_fwd(q, k, v, sinks, out, lse=None, *, window: int = 0, scale: float | None = None,
+             stream=None) -> None:
+    """O and LSE of causal (+ sliding-window) GQA attention with a per-head sink.
+
+    q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] (bf16 or fp32, same dtype), sinks [Hq] fp32 or
+    None, out [B,Hq,Lq,D] (bf16 or fp32), lse [B,Hq,Lq] fp32 or None.
+    """
+    import torch
+
+    B, Hq, Lq, D = q.shape
+    _, Hkv, Lk, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/k/v/out")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if sinks is not None and tuple(sinks.shape) != (Hq,):
+        raise ValueError("sinks must be [Hq]")
+    if lse is not None and tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("lse must be [B,Hq,Lq]")
+    if scale is None:
+        scale = D ** -0.5
+    rc = load_library().attn_fwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(sinks, "sinks", torch.float32),
+        _dev(out, "out"), _dev(lse, "lse", torch.float32), B, Hq, Hkv, Lq, Lk, D, int(window),
+        float(scale), _dtype_code(q), _dtype_code(out), _stream(stream))
+    _check("attn_fwd", rc)
+
+
+def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_part, *,
+                        window: int = 0, scale: float | None = None, stream=None) -> None:
+    """Per-split partial outputs and sink-free LSEs of one decode step.
+
+    q [B,Hq,1,D] bf16; caches [B,Hkv,Lk_max,D] bf16; seqlens_k, num_splits [B] int32;
+    o_part [B,Hq,max_splits,D] fp32; lse_part [B,Hq,max_splits] fp32.
+    """
+    import torch
+
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query per sequence: q must be [B,Hq,1,D]")
+    _, Hkv, Lk_max, _ = k_cache.shape
+    max_splits = o_part.shape[2]
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache shapes differ")
+    if tuple(o_part.shape) != (B, Hq, max_splits, D) or tuple(lse_part.shape) != (B, Hq, max_splits):
+        raise ValueError("o_part must be [B,Hq,max_splits,D] and lse_part [B,Hq,max_splits]")
+    if scale is None:
+        scale = D ** -0.5
+    rc = load_library().attn_decode_splitkv(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(seqlens_k, "seqlens_k", torch.int32), _dev(num_splits, "num_splits", torch.int32),
+        _dev(o_part, "o_part", torch.float32), _dev(lse_part, "lse_part", torch.float32),
+        B, Hq, Hkv, Lk_max, D, max_splits, int(window), float(scale), _dtype_code(q),
+        _stream(stream))
+    _check("attn_decode_splitkv", rc)
+
+
+def attn_combine(o_part, lse_part, seqlens_k, num_splits, sinks, out, lse=None, *, Lk_max: int,
+                 window: int = 0, stream=None) -> None:
+    """Merge the valid splits of each (b, h) and add the sink once.
+
+    out [B,Hq,1,D] (bf16 or fp32); lse [B,Hq] fp32 or None.  Lk_max and window
+    must be the values given to attn_decode_splitkv.
+    """
+    import torch
+
+    B, Hq, max_splits, D = o_part.shape
+    if tuple(out.shape) != (B, Hq, 1, D):
+        raise ValueError("out must be [B,Hq,1,D]")
+    if lse is not None and tuple(lse.shape) != (B, Hq):
+        raise ValueError("lse must be [B,Hq]")
+    rc = load_library().attn_combine(
+        _dev(o_part, "o_part", torch.float32), _dev(lse_part, "lse_part", torch.float32),
+        _dev(seqlens_k, "seqlens_k", torch.int32), _dev(num_splits, "num_splits", torch.int32),
+        _dev(sinks, "sinks", torch.float32), _dev(out, "out"), _dev(lse, "lse", torch.float32),
+        B, Hq, D, int(Lk_max), max_splits, int(window), _dtype_code(out), _stream(stream))
+    _check("attn_combine", rc)

@@ -1,0 +1,63 @@
+"""Build the gfx950 attention library: libattn_mi355x.so next to this file.
+
+Offline, in-tree, with hipcc only:  python -m exact_attention_attn_amd.build
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libattn_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_api.cpp"]
+ARCH = "gfx950"
+
+# Packed fp32 VALU instructions are kept out of the code object.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the HIP toolchain is required to build the library")
+    return path
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source for gfx950 and link the shared library; return its path."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [cc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
+               "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra_flags,
+               os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,336 @@
+// attn_decode.hip -- split-KV decode and the valid-split LSE combine (gfx950).
+//
+// Decode: one work-group per (split, KV head, query-column group, sequence).
+// The G = Hq/Hkv query heads that share a KV head are the columns of
+// S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each K/V byte of the split is
+// read from HBM once for all of them.  Tiles of 128 keys are staged through
+// LDS (registers prefetch the next tile while the current one is computed);
+// wave w scores keys [32w, 32w+32) of every tile with its own online-softmax
+// state, and the four states are merged through LDS at the end into the
+// split's normalised partial output and its sink-free LSE.
+//
+// Combine: one wave per (sequence, query head).  Lane s holds the LSE of
+// split s; only the n_valid splits that exist are loaded (FlashMLA patch
+// stack page, section 3: no masked work for splits that do not exist, real
+// splits accumulated in their order).  The sink joins as one more logit.
+#include "attn_common.hpp"
+#include "attn_kernels.hpp"
+
+namespace attn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeysPerWave = 32;
+constexpr int kTileKeys = kKeysPerWave * kWaves;  // 128
+constexpr float kRebaseThreshold = 8.0f;
+
+struct DecArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seqlens;
+  const int32_t* nsplits;
+  float* o_part;
+  float* lse_part;
+  int Hq, Hkv, Lk_max, max_splits, window, n_qgroups;
+  float c;  // scale * log2(e)
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
+  using Tile = BfTile<D>;
+  constexpr int TILE_BYTES = kTileKeys * Tile::kRowBytes;
+  constexpr int KS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int LOADS = TILE_BYTES / 16 / kThreads;
+  constexpr int MQ = 8;           // query columns merged per pass
+  constexpr int OPITCH = D + 4;   // floats per merged row in LDS
+  static_assert(kWaves * MQ * OPITCH * 4 + 2 * kWaves * MQ * 4 <= 2 * TILE_BYTES, "merge fits");
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * TILE_BYTES];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y % a.Hkv, qg = blockIdx.y / a.Hkv;
+  const int b = blockIdx.z;
+  const SplitRange sr = split_rule(a.seqlens[b], a.nsplits[b], a.Lk_max, a.max_splits, a.window);
+  if (s >= sr.n_valid) return;  // uniform over the work-group
+  const int k_begin = sr.lo + s * sr.chunk;
+  const int k_end = min(k_begin + sr.chunk, sr.Lk);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = a.Hq / a.Hkv;
+  const int qcol = qg * 32 + col;  // query head within the group
+  const bool col_valid = qcol < G;
+  const int h = kvh * G + qcol;
+
+  const uint16_t* kh = a.k + ((size_t)(b * a.Hkv + kvh) * a.Lk_max) * D;
+  const uint16_t* vh = a.v + ((size_t)(b * a.Hkv + kvh) * a.Lk_max) * D;
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 v = {0, 0, 0, 0};
+    if (col_valid) v = *(const u32x4*)(a.q + ((size_t)(b * a.Hq + h)) * D + ks * 16 + half * 8);
+    qf[ks] = as_bf16x8(v);
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
+  float m_run = kNegInf, l_run = 0.0f;
+
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int cid = threadIdx.x + i * kThreads;
+      int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
+      int key = t0 + r;
+      if (key < k_end) {
+        kreg[i] = *(const u32x4*)(kh + (size_t)key * D + cch * 8);
+        vreg[i] = *(const u32x4*)(vh + (size_t)key * D + cch * 8);
+      } else {
+        kreg[i] = (u32x4){0, 0, 0, 0};
+        vreg[i] = (u32x4){0, 0, 0, 0};
+      }
+    }
+  };
+  lds_char* ks_ = smem;
+  lds_char* vs_ = smem + TILE_BYTES;
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int cid = threadIdx.x + i * kThreads;
+      int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
+      int off = Tile::off(r, cch * 16);
+      lds_write16(ks_, off, kreg[i]);
+      lds_write16(vs_, off, vreg[i]);
+    }
+  };
+
+  const int k_row = wave * kKeysPerWave + key_perm(col);
+  const int tr_key = (lane & 15) >> 2;
+  const int tr_d = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  load_tile(k_begin);
+  for (int t0 = k_begin; t0 < k_end; t0 += kTileKeys) {
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    if (t0 + kTileKeys < k_end) load_tile(t0 + kTileKeys);
+    __syncthreads();
+    const int w0 = t0 + wave * kKeysPerWave;
+    if (w0 < k_end) {
+      f32x16 st = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 kf = as_bf16x8(lds_read16(ks_, Tile::off(k_row, (ks * 2 + half) * 16)));
+        st = mfma_32x32x16(kf, qf[ks], st);
+      }
+      float sv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] = st[v];
+      if (w0 + kKeysPerWave > k_end) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          sv[v] = (w0 + key_of_reg(v, half) < k_end) ? sv[v] : kNegInf;
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+      mx = pair_max(mx);
+      float m_new = fmaxf(m_run, mx * a.c);
+      bool need = m_new > m_run + kRebaseThreshold;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float alpha = need ? exp2_fast(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      }
+      float m_use = m_run == kNegInf ? 0.0f : m_run;
+      float sum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sv[v] = exp2_fast(__builtin_fmaf(sv[v], a.c, -m_use));
+        sum += sv[v];
+      }
+      l_run += sum;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const float* x = sv + s2 * 8;
+        pf[s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          int key = wave * kKeysPerWave + s2 * 16 + half * 8 + tr_key;
+          int dd = db * 32 + tr_d;
+          i16x4 lo = lds_read_tr16(vs_, Tile::off(key, dd * 2));
+          i16x4 hi = lds_read_tr16(vs_, Tile::off(key + 4, dd * 2));
+          o[db] = mfma_32x32x16(join_tr(lo, hi), pf[s2], o[db]);
+        }
+    }
+  }
+
+  // Merge the four per-wave states of each query column through LDS.
+  const float l_tot = pair_sum(l_run);
+  float* sm_o = (float*)smem_raw;                   // [wave][MQ][OPITCH]
+  float* sm_m = sm_o + kWaves * MQ * OPITCH;        // [wave][MQ]
+  float* sm_l = sm_m + kWaves * MQ;                 // [wave][MQ]
+  const int n_cols = min(32, G - qg * 32);
+  for (int c0 = 0; c0 < n_cols; c0 += MQ) {
+    __syncthreads();
+    if (col >= c0 && col < c0 + MQ && col < n_cols) {
+      int cq = col - c0;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int d = db * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          sm_o[(wave * MQ + cq) * OPITCH + d] = o[db][r];
+        }
+      if (half == 0) {
+        sm_m[wave * MQ + cq] = m_run;
+        sm_l[wave * MQ + cq] = l_tot;
+      }
+    }
+    __syncthreads();
+    const int ncq = min(MQ, n_cols - c0);
+    for (int idx = threadIdx.x; idx < ncq * D; idx += kThreads) {
+      int cq = idx / D, d = idx % D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * MQ + cq]);
+      float L = 0.0f, acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        float f = exp2_fast(sm_m[w * MQ + cq] - M);  // -inf (wave saw no key) -> 0
+        L += sm_l[w * MQ + cq] * f;
+        acc += sm_o[(w * MQ + cq) * OPITCH + d] * f;
+      }
+      int hh = kvh * G + qg * 32 + c0 + cq;
+      size_t base = ((size_t)(b * a.Hq + hh) * a.max_splits + s);
+      a.o_part[base * D + d] = acc / L;
+      if (d == 0) a.lse_part[base] = (M + log2_fast(L)) * kLn2;
+    }
+  }
+}
+
+struct CombArgs {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* seqlens;
+  const int32_t* nsplits;
+  const float* sinks;
+  void* out;
+  float* lse;
+  int B, Hq, Lk_max, max_splits, window;
+};
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombArgs a) {
+  constexpr int PER = D / 64;  // d values per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.x * kWaves + wave;
+  if (bh >= a.B * a.Hq) return;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const SplitRange sr = split_rule(a.seqlens[b], a.nsplits[b], a.Lk_max, a.max_splits, a.window);
+  const int n = sr.n_valid;
+  const size_t row = (size_t)bh * a.max_splits;
+
+  float ls = lane < n ? a.lse_part[row + lane] : kNegInf;
+  const float sig = a.sinks ? a.sinks[h] : kNegInf;
+  const float M = fmaxf(wave_max(ls), sig);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+  float lse_out = kNegInf, inv = 0.0f;
+  if (M != kNegInf) {
+    float w = lane < n ? exp2_fast((ls - M) * kLog2e) : 0.0f;
+    float den = wave_sum(w) + (a.sinks ? exp2_fast((sig - M) * kLog2e) : 0.0f);
+    const float* op = a.o_part + row * D + lane * PER;
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+      float x[4][PER];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[u][e] = op[(size_t)(s + u) * D + e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s + u));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(ws, x[u][e], acc[e]);
+      }
+    }
+    for (; s < n; ++s) {
+      float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s));
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(ws, op[(size_t)s * D + e], acc[e]);
+    }
+    inv = 1.0f / den;
+    lse_out = M + log2_fast(den) * kLn2;
+  }
+  if constexpr (OUT_F32) {
+    float* dst = (float*)a.out + (size_t)bh * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = acc[e] * inv;
+  } else {
+    uint16_t* dst = (uint16_t*)a.out + (size_t)bh * D + lane * PER;
+    if constexpr (PER == 2) {
+      *(uint32_t*)dst = pack2_bf16(acc[0] * inv, acc[1] * inv);
+    } else {
+      uint32_t pk = pack2_bf16(acc[0] * inv, 0.0f);
+      dst[0] = (uint16_t)(pk & 0xFFFF);
+    }
+  }
+  if (a.lse && lane == 0) a.lse[bh] = lse_out;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
+                         float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
+                         int max_splits, int window, float scale, hipStream_t stream) {
+  DecArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k_cache; a.v = (const uint16_t*)v_cache;
+  a.seqlens = seqlens_k; a.nsplits = num_splits; a.o_part = o_part; a.lse_part = lse_part;
+  a.Hq = Hq; a.Hkv = Hkv; a.Lk_max = Lk_max; a.max_splits = max_splits; a.window = window;
+  int G = Hq / Hkv;
+  a.n_qgroups = (G + 31) / 32;
+  a.c = scale * kLog2e;
+  dim3 grid(max_splits, Hkv * a.n_qgroups, B);
+  if (D == 128)
+    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, const int32_t* seqlens_k,
+                          const int32_t* num_splits, const float* sinks, void* out, float* lse,
+                          int B, int Hq, int D, int Lk_max, int max_splits, int window,
+                          bool out_f32, hipStream_t stream) {
+  CombArgs a;
+  a.o_part = o_part; a.lse_part = lse_part; a.seqlens = seqlens_k; a.nsplits = num_splits;
+  a.sinks = sinks; a.out = out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Lk_max = Lk_max; a.max_splits = max_splits; a.window = window;
+  dim3 grid((B * Hq + kWaves - 1) / kWaves);
+  if (D == 128) {
+    if (out_f32) hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

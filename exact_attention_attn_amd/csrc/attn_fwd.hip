@@ -1,0 +1,483 @@
+// attn_fwd.hip -- fused tiled exact-attention forward for gfx950 (MI355X).
+//
+// One work-group = 4 waves = 128 query rows of one (batch, query head); each
+// wave owns 32 rows.  K/V tiles of 64 keys of the head's KV head (GQA:
+// h / (Hq/Hkv)) stream HBM -> registers -> LDS (double-buffered, one barrier
+// per tile).  Per tile and wave:
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, K from LDS, Q^T held in VGPRs;
+//                   each lane owns one query column and 32 keys of it
+//   mask            only on tiles that cut the causal diagonal, the window
+//                   edge or the end of the keys
+//   online softmax  in the exp2 domain (running max m, partial sum l); the
+//                   accumulator is rebased only when the max grew by > 8
+//                   (2^8 headroom keeps every term finite in fp32)
+//   O^T += V^T P^T  V read from LDS with ds_read_b64_tr_b16, P in bf16 (RNE)
+// Finalise: the sink logit joins with the rebased update of the Flint page
+// ("fix two"): m' = max(m, sink*log2e), r = 2^(m - m'),
+// l' = l*r + 2^(sink*log2e - m'), O = acc*r/l', LSE = ln2*(m' + log2 l').
+//
+// The float32-input variant is the same algorithm on v_mfma_f32_32x32x2_f32
+// with 32-key tiles and an fp32 LDS layout.
+#include "attn_common.hpp"
+#include "attn_kernels.hpp"
+
+#include <type_traits>
+
+namespace attn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;
+constexpr int kBr = kRowsPerWave * kWaves;  // query rows per work-group
+constexpr float kRebaseThreshold = 8.0f;    // log2 headroom before the accumulator is rebased
+
+// Which key range a group of query rows needs, and how a tile relates to it.
+struct RowSpan {
+  int p_first, p_last;  // absolute positions of the first/last valid row
+};
+
+__device__ __forceinline__ int tile_kind(int t0, int bc, RowSpan s, int window, int Lk) {
+  // 0: no key of the tile is visible to any row; 1: every pair visible; 2: mixed
+  if (t0 > s.p_last) return 0;
+  if (window > 0 && t0 + bc - 1 <= s.p_first - window) return 0;
+  bool full = (t0 + bc - 1 <= s.p_first) && (t0 + bc <= Lk) &&
+              (window <= 0 || t0 >= s.p_last - window + 1);
+  return full ? 1 : 2;
+}
+
+// Online-softmax state of the query column a lane owns.
+struct Row {
+  float m;  // reference max (log2 domain) of acc and l; -inf before any visible key
+  float l;  // partial sum of this lane half
+};
+
+// Update the running state with a tile of raw scores s (already masked to -inf),
+// turn s into probabilities in place and return the rescale factor for acc.
+template <int N>
+__device__ __forceinline__ float softmax_tile(float (&s)[N], Row& row, float c) {
+  float mx = s[0];
+#pragma unroll
+  for (int v = 1; v < N; ++v) mx = fmaxf(mx, s[v]);
+  mx = pair_max(mx);
+  float m_new = fmaxf(row.m, mx * c);
+  float alpha = 1.0f;
+  bool need = m_new > row.m + kRebaseThreshold;  // false while m_new = -inf
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    alpha = need ? exp2_fast(row.m - m_new) : 1.0f;
+    row.m = need ? m_new : row.m;
+    row.l *= alpha;
+  }
+  float m_use = row.m == kNegInf ? 0.0f : row.m;
+  float sum = 0.0f;
+#pragma unroll
+  for (int v = 0; v < N; ++v) {
+    s[v] = exp2_fast(__builtin_fmaf(s[v], c, -m_use));
+    sum += s[v];
+  }
+  row.l += sum;
+  return alpha;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float a, float b, float cc, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float cc, float d) {
+  *(f32x4*)dst = (f32x4){a, b, cc, d};
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, float a, float b, float cc, float d) {
+  *(u32x2*)dst = (u32x2){pack2_bf16(a, b), pack2_bf16(cc, d)};
+}
+
+// Finalise with the sink and store O (4 consecutive d per register quad) and LSE.
+template <int NDB, typename OutT>
+__device__ __forceinline__ void finalize_store(const f32x16 (&o)[NDB], Row row, float sink_l2,
+                                               OutT* orow, float* lse_dst, bool valid, int half) {
+  float l_tot = pair_sum(row.l);
+  float m_fin = fmaxf(row.m, sink_l2);
+  float scale_o = 0.0f, lse = kNegInf;
+  if (m_fin != kNegInf) {
+    float r = exp2_fast(row.m - m_fin);  // row.m = -inf (no key) -> 0
+    float den = l_tot * r + exp2_fast(sink_l2 - m_fin);
+    scale_o = r / den;
+    lse = (m_fin + log2_fast(den)) * kLn2;
+  }
+  if (!valid) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int d = db * 32 + j * 8 + half * 4;
+      store4<OutT>(orow + d, o[db][j * 4 + 0] * scale_o, o[db][j * 4 + 1] * scale_o,
+                   o[db][j * 4 + 2] * scale_o, o[db][j * 4 + 3] * scale_o);
+    }
+  }
+  if (lse_dst && half == 0) *lse_dst = lse;
+}
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* sinks;
+  void* out;
+  float* lse;
+  int B, Hq, Hkv, Lq, Lk, window;
+  float c;  // scale * log2(e)
+  int n_qtiles;
+};
+
+// Decode the work-group id into (b, h, q-tile); longest q-tiles first within
+// each (batch, KV head), and the G query heads of a KV head adjacent.
+struct Work {
+  int b, h, kvh, qt;
+};
+__device__ __forceinline__ Work decode_work(const FwdArgs& a) {
+  int G = a.Hq / a.Hkv;
+  int total = a.n_qtiles * a.Hq * a.B;
+  int id = xcd_remap(blockIdx.x, total);
+  Work w;
+  int g = id % G;
+  id /= G;
+  w.qt = a.n_qtiles - 1 - id % a.n_qtiles;
+  id /= a.n_qtiles;
+  w.kvh = id % a.Hkv;
+  w.b = id / a.Hkv;
+  w.h = w.kvh * G + g;
+  return w;
+}
+
+// ------------------------------------------------------------------------
+// bf16 inputs
+// ------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+  using Tile = BfTile<D>;
+  constexpr int BC = 64;
+  constexpr int TILE_BYTES = BC * Tile::kRowBytes;
+  constexpr int KS = D / 16;   // k-steps of S^T
+  constexpr int NDB = D / 32;  // 32-wide d blocks of O^T
+  constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // 16 B loads per thread per tensor per tile
+  using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * TILE_BYTES];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const Work wk = decode_work(a);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int off_q = a.Lk - a.Lq;
+
+  const uint16_t* qh = (const uint16_t*)a.q + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq) * D;
+  const uint16_t* kh = (const uint16_t*)a.k + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
+  const uint16_t* vh = (const uint16_t*)a.v + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
+
+  // Rows of the work-group and of this wave.
+  const int r0 = wk.qt * kBr;
+  const int r_end = min(r0 + kBr, a.Lq);
+  RowSpan wg_span = {r0 + off_q, r_end - 1 + off_q};
+  const int w0 = r0 + wave * kRowsPerWave;
+  const bool wave_active = w0 < a.Lq;
+  RowSpan w_span = {w0 + off_q, min(w0 + kRowsPerWave, a.Lq) - 1 + off_q};
+
+  // Key tiles the work-group needs.
+  int key_lo = a.window > 0 ? max(0, wg_span.p_first - a.window + 1) : 0;
+  int key_hi = wg_span.p_last + 1;
+  const int t_begin = key_lo / BC, t_end = (key_hi + BC - 1) / BC;
+
+  // Q^T operand: lane holds query row w0+col, d = ks*16 + half*8 .. +8.
+  const int my_row = w0 + col;
+  const bool row_valid = my_row < a.Lq;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 v = {0, 0, 0, 0};
+    if (row_valid) v = *(const u32x4*)(qh + (size_t)my_row * D + ks * 16 + half * 8);
+    qf[ks] = as_bf16x8(v);
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
+  Row row = {kNegInf, 0.0f};
+
+  // Mask bounds of this lane's row: visible keys are [vis_lo, vis_hi].
+  const int p = my_row + off_q;
+  const int vis_hi = min(p, a.Lk - 1);
+  const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
+
+  // Staging: thread t moves 16 B chunks t + i*kThreads of each tile.
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int cid = threadIdx.x + i * kThreads;
+      int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
+      int key = t * BC + r;
+      if (key < a.Lk) {
+        kreg[i] = *(const u32x4*)(kh + (size_t)key * D + cch * 8);
+        vreg[i] = *(const u32x4*)(vh + (size_t)key * D + cch * 8);
+      } else {
+        kreg[i] = (u32x4){0, 0, 0, 0};
+        vreg[i] = (u32x4){0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    lds_char* ks_ = smem + buf * 2 * TILE_BYTES;
+    lds_char* vs_ = ks_ + TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int cid = threadIdx.x + i * kThreads;
+      int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
+      int off = Tile::off(r, cch * 16);
+      lds_write16(ks_, off, kreg[i]);
+      lds_write16(vs_, off, vreg[i]);
+    }
+  };
+
+  // Per-lane constant parts of the LDS addresses.
+  // K operand: row kb*32 + key_perm(col), bytes (ks*2 + half)*16.
+  const int k_row = key_perm(col);
+  // V^T operand via transposed reads: lane j of each 16-lane group addresses
+  // key (base + j/4), d = db*32 + ((lane/16)%2)*16 + (j%4)*4.
+  const int tr_key = (lane & 15) >> 2;
+  const int tr_d = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  if (t_begin < t_end) {
+    load_tile(t_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    const bool more = t + 1 < t_end;
+    if (more) load_tile(t + 1);
+
+    const int t0 = t * BC;
+    const int kind = wave_active ? tile_kind(t0, BC, w_span, a.window, a.Lk) : 0;
+    if (kind != 0) {
+      const lds_char* ks_ = smem + buf * 2 * TILE_BYTES;
+      const lds_char* vs_ = ks_ + TILE_BYTES;
+      f32x16 st[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 kf = as_bf16x8(lds_read16(ks_, Tile::off(kb * 32 + k_row, (ks * 2 + half) * 16)));
+          st[kb] = mfma_32x32x16(kf, qf[ks], st[kb]);
+        }
+      }
+      float s[32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb * 16 + v] = st[kb][v];
+      if (kind == 2) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            int j = t0 + kb * 32 + key_of_reg(v, half);
+            bool vis = (j >= vis_lo) & (j <= vis_hi);
+            s[kb * 16 + v] = vis ? s[kb * 16 + v] : kNegInf;
+          }
+      }
+      float alpha = softmax_tile<32>(s, row, a.c);
+      if (alpha != 1.0f) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      }
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const float* x = s + kb * 16 + s2 * 8;
+          pf[kb][s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+        }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            int key = kb * 32 + s2 * 16 + half * 8 + tr_key;
+            int dd = db * 32 + tr_d;
+            i16x4 lo = lds_read_tr16(vs_, Tile::off(key, dd * 2));
+            i16x4 hi = lds_read_tr16(vs_, Tile::off(key + 4, dd * 2));
+            o[db] = mfma_32x32x16(join_tr(lo, hi), pf[kb][s2], o[db]);
+          }
+      }
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float sink_l2 = a.sinks ? a.sinks[wk.h] * kLog2e : kNegInf;
+  OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row) * D;
+  float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row : nullptr;
+  finalize_store<NDB, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
+}
+
+// ------------------------------------------------------------------------
+// float32 inputs (v_mfma_f32_32x32x2_f32)
+// ------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
+  constexpr int BC = 32;
+  constexpr int PITCH = D + 1;  // floats per LDS row (odd pitch spreads rows over banks)
+  constexpr int TILE_FLOATS = BC * PITCH;
+  constexpr int KS = D / 2;
+  constexpr int NDB = D / 32;
+  constexpr int LOADS = BC * D / 4 / kThreads;
+  using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
+
+  __shared__ float smem[2][TILE_FLOATS];  // [K/V]; single buffer, registers prefetch
+
+  const Work wk = decode_work(a);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int off_q = a.Lk - a.Lq;
+
+  const float* qh = (const float*)a.q + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq) * D;
+  const float* kh = (const float*)a.k + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
+  const float* vh = (const float*)a.v + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
+
+  const int r0 = wk.qt * kBr;
+  const int r_end = min(r0 + kBr, a.Lq);
+  RowSpan wg_span = {r0 + off_q, r_end - 1 + off_q};
+  const int w0 = r0 + wave * kRowsPerWave;
+  const bool wave_active = w0 < a.Lq;
+  RowSpan w_span = {w0 + off_q, min(w0 + kRowsPerWave, a.Lq) - 1 + off_q};
+  int key_lo = a.window > 0 ? max(0, wg_span.p_first - a.window + 1) : 0;
+  int key_hi = wg_span.p_last + 1;
+  const int t_begin = key_lo / BC, t_end = (key_hi + BC - 1) / BC;
+
+  const int my_row = w0 + col;
+  const bool row_valid = my_row < a.Lq;
+  float qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = row_valid ? qh[(size_t)my_row * D + ks * 2 + half] : 0.0f;
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
+  Row row = {kNegInf, 0.0f};
+  const int p = my_row + off_q;
+  const int vis_hi = min(p, a.Lk - 1);
+  const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
+
+  f32x4 kreg[LOADS], vreg[LOADS];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int cid = threadIdx.x + i * kThreads;
+      int r = cid / (D / 4), c4 = cid % (D / 4);
+      int key = t * BC + r;
+      if (key < a.Lk) {
+        kreg[i] = *(const f32x4*)(kh + (size_t)key * D + c4 * 4);
+        vreg[i] = *(const f32x4*)(vh + (size_t)key * D + c4 * 4);
+      } else {
+        kreg[i] = (f32x4){0, 0, 0, 0};
+        vreg[i] = (f32x4){0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int cid = threadIdx.x + i * kThreads;
+      int r = cid / (D / 4), c4 = cid % (D / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        smem[0][r * PITCH + c4 * 4 + e] = kreg[i][e];
+        smem[1][r * PITCH + c4 * 4 + e] = vreg[i][e];
+      }
+    }
+  };
+
+  const int k_row = key_perm(col);
+  if (t_begin < t_end) load_tile(t_begin);
+  for (int t = t_begin; t < t_end; ++t) {
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    if (t + 1 < t_end) load_tile(t + 1);
+    __syncthreads();
+    const int t0 = t * BC;
+    const int kind = wave_active ? tile_kind(t0, BC, w_span, a.window, a.Lk) : 0;
+    if (kind != 0) {
+      const float* ks_ = smem[0];
+      const float* vs_ = smem[1];
+      f32x16 st = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) st = mfma_32x32x2(ks_[k_row * PITCH + ks * 2 + half], qf[ks], st);
+      float s[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = st[v];
+      if (kind == 2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int j = t0 + key_of_reg(v, half);
+          bool vis = (j >= vis_lo) & (j <= vis_hi);
+          s[v] = vis ? s[v] : kNegInf;
+        }
+      }
+      float alpha = softmax_tile<16>(s, row, a.c);
+      if (alpha != 1.0f) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      }
+      // O^T += V^T P^T, 2 keys per step: step u takes register u of each half.
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          int key = key_of_reg(u, half);
+          o[db] = mfma_32x32x2(vs_[key * PITCH + db * 32 + col], s[u], o[db]);
+        }
+    }
+  }
+
+  const float sink_l2 = a.sinks ? a.sinks[wk.h] * kLog2e : kNegInf;
+  OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row) * D;
+  float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row : nullptr;
+  finalize_store<NDB, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
+}
+
+template <typename K>
+hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream) {
+  int total = a.n_qtiles * a.Hq * a.B;
+  hipLaunchKernelGGL(kernel, dim3(total), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* sinks, void* out,
+                      float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int D, int window,
+                      float scale, bool in_f32, bool out_f32, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.out = out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.window = window;
+  a.c = scale * kLog2e;
+  a.n_qtiles = (Lq + kBr - 1) / kBr;
+  if (!in_f32) {
+    if (D == 128) return out_f32 ? launch(fwd_bf16_kernel<128, true>, a, stream)
+                                 : launch(fwd_bf16_kernel<128, false>, a, stream);
+    return out_f32 ? launch(fwd_bf16_kernel<64, true>, a, stream)
+                   : launch(fwd_bf16_kernel<64, false>, a, stream);
+  }
+  if (D == 128) return out_f32 ? launch(fwd_f32_kernel<128, true>, a, stream)
+                               : launch(fwd_f32_kernel<128, false>, a, stream);
+  return out_f32 ? launch(fwd_f32_kernel<64, true>, a, stream)
+                 : launch(fwd_f32_kernel<64, false>, a, stream);
+}
+
+int fwd_grid_size(int B, int Hq, int Lq) { return ((Lq + kBr - 1) / kBr) * Hq * B; }
+
+}  // namespace attn

@@ -1,0 +1,131 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * Three calls form the path:
+ *   attn_fwd             fused tiled attention forward (prefill): causal +
+ *                        sliding window, GQA, learned per-head sink, LSE;
+ *   attn_decode_splitkv  split-KV decode: per-split partial outputs and LSEs;
+ *   attn_combine         LSE-weighted merge of the valid splits, sink added once.
+ *
+ * Conventions shared by every call
+ *  - Tensor pointers are HIP device pointers, owned by the caller, contiguous
+ *    in the stated layout, and 16-byte aligned.  The library allocates no
+ *    device or host memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work and return; ordering is the stream's.
+ *  - Return value: ATTN_OK (0) or a positive ATTN_ERR_* code.  On an error
+ *    nothing is launched.  Faults inside a kernel surface at the caller's
+ *    next synchronisation, not here.
+ *  - Element types: ATTN_BF16 (bfloat16) or ATTN_F32 for inputs (attn_fwd
+ *    only; decode is bf16) and for outputs.  Accumulation is float32.
+ *  - Masking (flash-attention repository profile, section 1 "capabilities":
+ *    causal and sliding-window masks; Flint page: every token sees only the
+ *    most recent 513 tokens): query row i of Lq sits at absolute position
+ *    p = i + Lk - Lq (the queries are the last Lq positions) and sees key j
+ *    iff j <= p and, when window > 0, j > p - window.  window <= 0: causal
+ *    only.  The window counts the query's own key.
+ *  - Sink (Flint page, "fix two"): sinks[h] is a logit of query head h in
+ *    the same units as scale*<q,k>; it joins the softmax denominator and has
+ *    no value vector:  O = sum_j e^{s_j - M} v_j / (sum_j e^{s_j - M} + e^{sink - M}).
+ *    The kernels apply it with the rebased update (new max = max(content
+ *    max, sink), every exponential <= 1), so it cannot overflow.
+ *  - LSE is the natural-log sum of exponentials, the sink included.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ATTN_BF16 = 0, ATTN_F32 = 1 };
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  ATTN_ERR_SHAPE = 2,       /* a size < 1 (Lq, Lk, B, heads), Hq % Hkv != 0,
+                               Lq > Lk, max_splits outside [1, 64], or an
+                               index space that overflows 64-bit offsets     */
+  ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64/128, unknown or unsupported dtype */
+  ATTN_ERR_VALUE = 4,       /* scale not finite and > 0, or a misaligned pointer */
+  ATTN_ERR_HIP = 5          /* the HIP runtime rejected a launch              */
+};
+
+#define ATTN_SPLIT_ALIGN 64  /* split boundaries: multiples of 64 keys from the window start */
+#define ATTN_MAX_SPLITS 64
+
+/*
+ * attn_fwd -- O = softmax(scale * Q K^T + mask, sink) V, and LSE.
+ *
+ * q    [B, Hq,  Lq, D]  in_dtype
+ * k, v [B, Hkv, Lk, D]  in_dtype; query head h reads KV head h / (Hq/Hkv)
+ * sinks [Hq] float32, or NULL for no sink
+ * out  [B, Hq,  Lq, D]  out_dtype
+ * lse  [B, Hq,  Lq]     float32, or NULL to skip
+ * D in {64, 128}; window <= 0 means none; scale > 0 (e.g. 1/sqrt(D)).
+ * A row that sees no key gets O = 0 and LSE = sink (or -inf without one).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, const float* sinks, void* out,
+             float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int D, int window, float scale,
+             int in_dtype, int out_dtype, void* stream);
+
+/*
+ * attn_decode_splitkv -- one query per sequence over a KV cache, cut into splits.
+ *
+ * Split-KV decode (flash-attention profile: split-KV benchmarks; FlashMLA
+ * patch stack page: split kernel + combine).  Sequence b's single query sits
+ * at position seqlens_k[b] - 1 and sees keys [lo, Lk), lo = max(0, Lk - window)
+ * (window <= 0: lo = 0).  With n = Lk - lo and ns = num_splits[b]:
+ *   chunk   = round_up(ceil(n / ns), 64),  n_valid = ceil(n / chunk) (<= ns),
+ *   split s covers [lo + s*chunk, min(lo + (s+1)*chunk, Lk)),  s < n_valid.
+ * For each valid split the kernel writes, for every query head h,
+ *   lse_part[b,h,s] = ln sum_{j in split} e^{s_j}          (no sink)
+ *   o_part[b,h,s,:] = sum_{j in split} e^{s_j - lse} v_j   (normalised)
+ * Lanes s >= n_valid are neither written nor ever read.
+ *
+ * q        [B, Hq, 1, D]        bf16
+ * k_cache, v_cache [B, Hkv, Lk_max, D] bf16; rows >= seqlens_k[b] are never read
+ * seqlens_k [B] int32 device, clamped in-kernel to [0, Lk_max]
+ * num_splits [B] int32 device, clamped in-kernel to [1, max_splits]
+ * o_part   [B, Hq, max_splits, D] float32 (caller-owned workspace)
+ * lse_part [B, Hq, max_splits]    float32
+ * max_splits in [1, 64]; in_dtype must be ATTN_BF16.
+ */
+int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
+                        float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
+                        int max_splits, int window, float scale, int in_dtype, void* stream);
+
+/*
+ * attn_combine -- merge the valid split partials of each (b, h), sink once.
+ *
+ * Exact small-split combine (FlashMLA patch stack page, section 3): only the
+ * n_valid lanes that exist are read (n_valid recomputed from seqlens_k,
+ * num_splits and window by the rule above), in order s = 0, 1, ...:
+ *   M = max(max_s lse_s, sink); w_s = e^{lse_s - M};
+ *   den = sum_s w_s + e^{sink - M};  O = sum_s w_s O_s / den;  LSE = M + ln den.
+ * The sink enters here and only here, as one more logit with a zero value.
+ *
+ * o_part, lse_part as written by attn_decode_splitkv; seqlens_k, num_splits,
+ * Lk_max, max_splits and window must be the values given to that call.
+ * sinks [Hq] float32 or NULL;  out [B, Hq, 1, D] out_dtype;  lse [B, Hq] or NULL
+ * A sequence with no visible key gets O = 0 and LSE = sink (-inf without one).
+ */
+int attn_combine(const float* o_part, const float* lse_part, const int32_t* seqlens_k,
+                 const int32_t* num_splits, const float* sinks, void* out, float* lse, int B,
+                 int Hq, int D, int Lk_max, int max_splits, int window, int out_dtype,
+                 void* stream);
+
+/* Human-readable name of an ATTN_* return code (static string). */
+const char* attn_strerror(int code);
+
+/* Library version, "attn-mi355x <major>.<minor>". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

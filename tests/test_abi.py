@@ -1,0 +1,117 @@
+"""CPU checks of the C ABI: the library loads, exports what include/attn.h
+declares, and rejects bad arguments on the host before any launch.
+
+Every call here fails validation, so no kernel is launched and no GPU is
+needed.  Pointers are fake (never dereferenced) and 256-byte aligned.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_attn_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x10000  # fake, aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.library_path()):
+        pytest.fail("libattn_mi355x.so not built: run `python -m exact_attention_attn_amd.build`")
+    return A.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"attn_fwd", "attn_decode_splitkv", "attn_combine", "attn_strerror",
+                          "attn_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.attn_version().decode().startswith("attn-mi355x")
+
+
+def test_strerror(lib):
+    for code in range(6):
+        assert lib.attn_strerror(code)
+    assert b"unknown" in lib.attn_strerror(99)
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, sinks=P, out=P, lse=P, B=1, Hq=8, Hkv=2, Lq=10, Lk=10, D=128,
+             window=0, scale=0.1, ind=0, outd=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["sinks"], a["out"], a["lse"], a["B"], a["Hq"],
+                        a["Hkv"], a["Lq"], a["Lk"], a["D"], a["window"], a["scale"], a["ind"],
+                        a["outd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
+    (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Lq=0), 2), (dict(Lk=0), 2),
+    (dict(Hq=7), 2), (dict(Lq=11), 2), (dict(B=1 << 30, Hq=64, Hkv=8, Lq=1 << 20, Lk=1 << 20), 2),
+    (dict(D=96), 3), (dict(D=256), 3), (dict(ind=2), 3), (dict(outd=-1), 3),
+    (dict(scale=0.0), 4), (dict(scale=-1.0), 4), (dict(scale=float("inf")), 4),
+    (dict(scale=float("nan")), 4), (dict(q=P + 8), 4), (dict(out=P + 2), 4), (dict(lse=P + 2), 4),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def dec(lib, **kw):
+    a = dict(q=P, k=P, v=P, sl=P, ns=P, op=P, lp=P, B=4, Hq=8, Hkv=2, Lk=100, D=128, ms=64,
+             window=0, scale=0.1, ind=0, stream=None)
+    a.update(kw)
+    return lib.attn_decode_splitkv(a["q"], a["k"], a["v"], a["sl"], a["ns"], a["op"], a["lp"],
+                                   a["B"], a["Hq"], a["Hkv"], a["Lk"], a["D"], a["ms"],
+                                   a["window"], a["scale"], a["ind"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(sl=None), 1), (dict(ns=None), 1), (dict(op=None), 1), (dict(lp=None), 1),
+    (dict(B=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(ms=0), 2), (dict(ms=65), 2), (dict(Lk=0), 2),
+    (dict(D=80), 3), (dict(ind=1), 3), (dict(scale=0.0), 4), (dict(k=P + 4), 4), (dict(sl=P + 2), 4),
+])
+def test_decode_rejects(lib, kw, code):
+    assert dec(lib, **kw) == code
+
+
+def comb(lib, **kw):
+    a = dict(op=P, lp=P, sl=P, ns=P, sinks=P, out=P, lse=P, B=4, Hq=8, D=128, Lk=100, ms=64,
+             window=0, outd=0, stream=None)
+    a.update(kw)
+    return lib.attn_combine(a["op"], a["lp"], a["sl"], a["ns"], a["sinks"], a["out"], a["lse"],
+                            a["B"], a["Hq"], a["D"], a["Lk"], a["ms"], a["window"], a["outd"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), 1), (dict(out=None), 1), (dict(sl=None), 1),
+    (dict(B=0), 2), (dict(ms=0), 2), (dict(ms=100), 2), (dict(Lk=0), 2),
+    (dict(D=32), 3), (dict(outd=7), 3), (dict(out=P + 8), 4), (dict(sinks=P + 1), 4),
+])
+def test_combine_rejects(lib, kw, code):
+    assert comb(lib, **kw) == code
+
+
+def test_python_binding_raises_on_error_code(lib):
+    with pytest.raises(A.AttnError) as e:
+        A._check("attn_fwd", 2)
+    assert e.value.code == 2 and "shape" in str(e.value)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.attn_fwd(q, k, k, None, q.clone())

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bar (bf16 inputs, fp32 accumulation, O read in fp32): max|dO| <= 1e-2,
+mean|dO| <= 1e-3, |dLSE| <= 1e-3.  Reduced sizes are compared element by
+element; full sizes on sampled rows that the oracle computes one by one.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_attn_amd import workloads as W
+
+gpu_util = pytest.importorskip("gpu_util")
+from gpu_util import compare, host_values, run_decode, run_fwd, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def full_oracle(q, k, v, sinks, dtype, window, scale):
+    return oracle.attention_fwd(host_values(q, dtype), host_values(k, dtype), host_values(v, dtype),
+                                sinks, window, scale)
+
+
+# --- the five workloads ---------------------------------------------------------
+
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_tiny_prefill(gpu, out_f32):
+    w = W.TINY_PREFILL
+    q, k, v, s = W.prefill_inputs(w)
+    say(f"tiny_prefill out_f32={out_f32}")
+    o, l = run_fwd(q, k, v, s, w.dtype, w.window, w.scale, out_f32=out_f32)
+    o_ref, l_ref = full_oracle(q, k, v, s, w.dtype, w.window, w.scale)
+    compare(o, l, o_ref, l_ref, "tiny_prefill", bf16_out=not out_f32)
+    # head 1 has sink +100: finite, tiny output and LSE ~ 100
+    assert np.abs(o[0, 1]).max() < 1e-30 and np.abs(l[0, 1] - 100.0).max() < 1e-3
+
+
+@pytest.mark.parametrize("name,L", [("swa_prefill", 1000), ("causal_prefill", 700),
+                                    ("long_swa_prefill", 1500)])
+def test_workload_reduced_length(gpu, name, L):
+    w = W.WORKLOADS[name]
+    q, k, v, s = W.prefill_inputs(w, L=L)
+    say(f"{name} L={L}")
+    o, l = run_fwd(q, k, v, s, w.dtype, w.window, w.scale)
+    o_ref, l_ref = full_oracle(q, k, v, s, w.dtype, w.window, w.scale)
+    compare(o, l, o_ref, l_ref, f"{name} L={L}")
+
+
+def sample_rows(L: int, seed: int, n_random=96):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 511, 512, 513, 514, 1023, 1024, 1025]
+    rows = set(r for r in fixed if r < L)
+    rows.update(range(max(0, L - 70), L))
+    rows.update(int(x) for x in rng.integers(0, L, n_random))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["swa_prefill", "causal_prefill", "long_swa_prefill"])
+def test_workload_full_size_sampled(gpu, name):
+    w = W.WORKLOADS[name]
+    say(f"{name} full size: generating inputs")
+    q, k, v, s = W.prefill_inputs(w)
+    heads = sorted({0, 1, w.Hq // 2 + 3, w.Hq - 1})  # includes forced-sink heads where present
+    picks = [(b, h, sample_rows(w.L, 7 * b + h)) for b in sorted({0, w.B - 1}) for h in heads]
+    say(f"{name} full size: running")
+    res = run_fwd(q, k, v, s, w.dtype, w.window, w.scale, rows=picks)
+    for (b, h, rows), (o, l) in zip(picks, res):
+        o_ref, l_ref = _rows_oracle(q, k, v, s, w, b, h, rows)
+        compare(o, l, o_ref, l_ref, f"{name} b={b} h={h}")
+
+
+def _rows_oracle(q, k, v, s, w, b, h, rows):
+    G = w.Hq // w.Hkv
+    kvh = h // G
+    qs = host_values(q[b:b + 1, h:h + 1], w.dtype)
+    ks = host_values(k[b:b + 1, kvh:kvh + 1], w.dtype)
+    vs = host_values(v[b:b + 1, kvh:kvh + 1], w.dtype)
+    return oracle.attention_rows(qs, ks, vs, s[h:h + 1], 0, 0, rows, w.window, w.scale)
+
+
+# --- edges -------------------------------------------------------------------------
+
+EDGE_L = [1, 2, 63, 64, 65, 127, 129, 257, 1000]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("L", EDGE_L)
+def test_edge_lengths(gpu, D, L):
+    rng = np.random.default_rng(L * 7 + D)
+    for (Hq, Hkv) in ((2, 2), (4, 2), (8, 1)):
+        for window in (0, 1, 2, 512, 513, 514, L + 5):
+            q = W.f32_to_bf16_bits(rng.standard_normal((1, Hq, L, D), dtype=np.float32))
+            k = W.f32_to_bf16_bits(rng.standard_normal((1, Hkv, L, D), dtype=np.float32))
+            v = W.f32_to_bf16_bits(rng.standard_normal((1, Hkv, L, D), dtype=np.float32))
+            sinks = np.array([-30.0, 0.0, 20.0, 100.0, 1.5, -2.0, 3.0, 0.5][:Hq], np.float32)
+            o, l = run_fwd(q, k, v, sinks, W.BF16, window, D ** -0.5)
+            o_ref, l_ref = full_oracle(q, k, v, sinks, W.BF16, window, D ** -0.5)
+            compare(o, l, o_ref, l_ref, f"L={L} D={D} H={Hq}/{Hkv} W={window}")
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (1, 300), (37, 300), (128, 1000), (200, 201), (129, 4000)])
+@pytest.mark.parametrize("window", [0, 513, 100])
+def test_fewer_queries_than_keys(gpu, Lq, Lk, window):
+    rng = np.random.default_rng(Lq * 31 + Lk)
+    D = 128
+    q = W.f32_to_bf16_bits(rng.standard_normal((2, 4, Lq, D), dtype=np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((2, 2, Lk, D), dtype=np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((2, 2, Lk, D), dtype=np.float32))
+    sinks = np.array([0.3, -1.0, 25.0, 2.0], np.float32)
+    o, l = run_fwd(q, k, v, sinks, W.BF16, window, D ** -0.5)
+    o_ref, l_ref = full_oracle(q, k, v, sinks, W.BF16, window, D ** -0.5)
+    compare(o, l, o_ref, l_ref, f"Lq={Lq} Lk={Lk} W={window}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_no_sink_and_large_scores(gpu, D):
+    rng = np.random.default_rng(D)
+    L = 300
+    # scores ~ N(0, 16): far more peaked than N(0,1) inputs give.  P is rounded
+    # to bf16 while the denominator sums the fp32 values, so a single dominant
+    # key carries up to 2^-9 relative error into O; std 16 scores exceed 1e-2.
+    q = W.f32_to_bf16_bits(rng.standard_normal((1, 2, L, D), dtype=np.float32) * 2)
+    k = W.f32_to_bf16_bits(rng.standard_normal((1, 1, L, D), dtype=np.float32) * 2)
+    v = W.f32_to_bf16_bits(rng.standard_normal((1, 1, L, D), dtype=np.float32))
+    for window in (0, 77):
+        o, l = run_fwd(q, k, v, None, W.BF16, window, D ** -0.5)
+        o_ref, l_ref = full_oracle(q, k, v, None, W.BF16, window, D ** -0.5)
+        compare(o, l, o_ref, l_ref, f"no sink, scores ~N(0, 16) W={window}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_f32_inputs(gpu, D):
+    rng = np.random.default_rng(D + 1)
+    L = 333
+    q = rng.standard_normal((2, 4, L, D), dtype=np.float32)
+    k = rng.standard_normal((2, 2, L, D), dtype=np.float32)
+    v = rng.standard_normal((2, 2, L, D), dtype=np.float32)
+    sinks = np.array([100.0, -1.0, 0.0, 20.0], np.float32)
+    for window in (0, 5, 200):
+        o, l = run_fwd(q, k, v, sinks, W.F32, window, D ** -0.5)
+        o_ref, l_ref = full_oracle(q, k, v, sinks, W.F32, window, D ** -0.5)
+        compare(o, l, o_ref, l_ref, f"f32 D={D} W={window}")
+
+
+def test_bf16_output(gpu):
+    w = W.SWA_PREFILL
+    q, k, v, s = W.prefill_inputs(w, L=600)
+    o, l = run_fwd(q, k, v, s, w.dtype, w.window, w.scale, out_f32=False)
+    o_ref, l_ref = full_oracle(q, k, v, s, w.dtype, w.window, w.scale)
+    compare(o, l, o_ref, l_ref, "bf16 out", bf16_out=True)
+
+
+def test_deterministic(gpu):
+    w = W.CAUSAL_PREFILL
+    q, k, v, s = W.prefill_inputs(w, L=777)
+    runs = [run_fwd(q, k, v, s, w.dtype, w.window, w.scale) for _ in range(5)]
+    for o, l in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1])
+
+
+# --- split-KV decode + combine ----------------------------------------------------------
+
+def decode_oracle(q, kc, vc, seqlens, nsplits, sinks, window, scale):
+    qf, kf, vf = (host_values(x, W.BF16) for x in (q, kc, vc))
+    op, lp, nv = oracle.decode_partials(qf, kf, vf, seqlens, nsplits, window, scale)
+    o, l = oracle.combine(op, lp, nv, sinks)
+    return op, lp, nv, o, l
+
+
+def check_decode(q, kc, vc, seqlens, nsplits, sinks, window, what):
+    D = q.shape[-1]
+    scale = D ** -0.5
+    op, lp, o, l = run_decode(q, kc, vc, seqlens, nsplits, sinks, window, scale)
+    op_r, lp_r, nv, o_r, l_r = decode_oracle(q, kc, vc, seqlens, nsplits, sinks, window, scale)
+    for b in range(q.shape[0]):
+        n = int(nv[b])
+        # valid lanes match the oracle's partials; the rest were never written
+        compare(op[b, :, :n], lp[b, :, :n], op_r[b, :, :n], lp_r[b, :, :n], f"{what} partials b={b}")
+        assert np.isnan(op[b, :, n:]).all() and np.isnan(lp[b, :, n:]).all(), f"{what}: lane >= n_valid written"
+    compare(o, l, o_r, l_r, what)
+    # the unsplit oracle agrees too (split + combine = unsplit)
+    ou, lu = oracle.decode(*(host_values(x, W.BF16) for x in (q, kc, vc)), seqlens, sinks, window, scale)
+    compare(o, l, ou, lu, what + " vs unsplit")
+    return o, l
+
+
+@pytest.mark.parametrize("splits", ["policy", "random"])
+def test_decode_reduced(gpu, splits):
+    w = W.SPLITKV_DECODE
+    q, kc, vc, seqlens, ns, s = W.decode_inputs(w, B=12, Lk_max=4096, random_splits=splits == "random")
+    seqlens[:4] = [1, 63, 64, 65]
+    say(f"decode reduced splits={splits}")
+    check_decode(q, kc, vc, seqlens, ns, s, 0, f"decode {splits}")
+
+
+@pytest.mark.parametrize("ns", [1, 2, 31, 32, 33, 63, 64])
+@pytest.mark.parametrize("window", [0, 513])
+def test_decode_split_counts(gpu, ns, window):
+    rng = np.random.default_rng(ns * 3 + window)
+    B, Hq, Hkv, D, Lmax = 6, 16, 2, 128, 2500
+    seqlens = np.array([1, 64, 65, 1024, 1025, 2500], np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, 1, D), dtype=np.float32))
+    kc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 40 + ns, 1, lengths=seqlens)
+    vc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 40 + ns, 2, lengths=seqlens)
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    sinks[0] = 30.0
+    check_decode(q, kc, vc, seqlens, np.full(B, ns, np.int32), sinks, window, f"ns={ns} W={window}")
+
+
+@pytest.mark.parametrize("G,D", [(1, 128), (8, 64), (40, 128), (64, 64)])
+def test_decode_head_groups(gpu, G, D):
+    rng = np.random.default_rng(G + D)
+    B, Hkv, Lmax = 3, 2, 700
+    Hq = G * Hkv
+    seqlens = np.array([700, 5, 333], np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, 1, D), dtype=np.float32))
+    kc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, G, 1, lengths=seqlens)
+    vc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, G, 2, lengths=seqlens)
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    check_decode(q, kc, vc, seqlens, np.array([3, 1, 64], np.int32), sinks, 0, f"G={G} D={D}")
+
+
+def test_decode_empty_sequence_and_no_sink(gpu):
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, D, Lmax = 3, 8, 1, 128, 256
+    seqlens = np.array([0, 256, 17], np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, 1, D), dtype=np.float32))
+    kc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 9, 1, lengths=seqlens)
+    vc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 9, 2, lengths=seqlens)
+    for sinks in (None, rng.standard_normal(Hq).astype(np.float32)):
+        op, lp, o, l = run_decode(q, kc, vc, seqlens, np.array([4, 4, 4], np.int32), sinks, 0, D ** -0.5)
+        assert np.array_equal(o[0], np.zeros((Hq, D)))
+        want = np.full(Hq, -np.inf) if sinks is None else sinks
+        assert np.array_equal(l[0], want.astype(np.float32))
+        _, _, nv, o_r, l_r = decode_oracle(q, kc, vc, seqlens, np.array([4, 4, 4]), sinks, 0, D ** -0.5)
+        compare(o[1:], l[1:], o_r[1:], l_r[1:], f"decode sinks={'none' if sinks is None else 'yes'}")
+
+
+def test_decode_matches_forward_with_one_query(gpu):
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, D, L = 2, 16, 2, 128, 3000
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, 1, D), dtype=np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    for window in (0, 513):
+        _, _, o, l = run_decode(q, k, v, np.array([L, L], np.int32), np.array([7, 64], np.int32),
+                                sinks, window, D ** -0.5)
+        of, lf = run_fwd(q, k, v, sinks, W.BF16, window, D ** -0.5)
+        compare(o, l, of[:, :, 0].astype(np.float64), lf[:, :, 0].astype(np.float64),
+                f"decode vs fwd W={window}", tol_max=2e-3, tol_mean=2e-4, tol_lse=2e-4)
+
+
+@pytest.mark.timeout(900)
+def test_decode_full_size(gpu):
+    w = W.SPLITKV_DECODE
+    say("splitkv_decode full size: generating inputs")
+    q, kc, vc, seqlens, ns, s = W.decode_inputs(w)
+    say("splitkv_decode full size: running")
+    op, lp, o, l = run_decode(q, kc, vc, seqlens, ns, s, 0, w.scale)
+    del op, lp
+    picks = [0, 1, 17, 31, 48, 63]
+    qf = host_values(q[picks], W.BF16)
+    kf = host_values(kc[picks], W.BF16)
+    vf = host_values(vc[picks], W.BF16)
+    o_r, l_r = oracle.decode(qf, kf, vf, seqlens[picks], s, 0, w.scale)
+    compare(o[picks], l[picks], o_r, l_r, "splitkv_decode full size")
