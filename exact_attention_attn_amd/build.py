@@ -18,6 +18,11 @@ LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_api.cpp"]
+# Per-source code-generation options.  The forward kernel keeps its MFMA
+# accumulators in architectural VGPRs: the softmax rescales them with VALU
+# instructions, and accumulators in AGPRs would be copied back and forth
+# around that (rarely taken) branch on every tile.
+SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the code object.
@@ -40,7 +45,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         cmd = [cc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
-               "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra_flags,
+               "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags,
                os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]

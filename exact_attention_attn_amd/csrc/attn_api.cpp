@@ -39,6 +39,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, int 
   // grid: one work-group per 128 query rows of each (batch, head)
   if ((long long)((Lq + 127) / 128) * Hq * B >= (1LL << 31)) return ATTN_ERR_SHAPE;
   if ((long long)B * Hq >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  // K/V rows of one head are addressed with 32-bit byte offsets.
+  if ((long long)Lk * D * 4 >= (1LL << 32)) return ATTN_ERR_SHAPE;
   if (!supported_dim(D) || !dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return ATTN_ERR_UNSUPPORTED;
   if (!(std::isfinite(scale) && scale > 0.0f)) return ATTN_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_VALUE;

@@ -29,6 +29,10 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __attribute__((address_space(3))) char lds_char;
 
+// s_waitcnt immediate that waits for every outstanding vector-memory load
+// (vmcnt = 0) and leaves the export and LDS counters unconstrained.
+constexpr int kWaitVmcnt0 = (7 << 4) | (0xF << 8);
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

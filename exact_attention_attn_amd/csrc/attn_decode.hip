@@ -60,7 +60,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   const int k_begin = sr.lo + s * sr.chunk;
   const int k_end = min(k_begin + sr.chunk, sr.Lk);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int G = a.Hq / a.Hkv;
   const int qcol = qg * 32 + col;  // query head within the group
@@ -89,14 +90,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
     for (int i = 0; i < LOADS; ++i) {
       int cid = threadIdx.x + i * kThreads;
       int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
-      int key = t0 + r;
-      if (key < k_end) {
-        kreg[i] = *(const u32x4*)(kh + (size_t)key * D + cch * 8);
-        vreg[i] = *(const u32x4*)(vh + (size_t)key * D + cch * 8);
-      } else {
-        kreg[i] = (u32x4){0, 0, 0, 0};
-        vreg[i] = (u32x4){0, 0, 0, 0};
-      }
+      // Rows past the split are loaded from its last key: they are masked
+      // (p = 0) and finite, so they add nothing.  Rows >= Lk are never read.
+      int key = min(t0 + r, k_end - 1);
+      kreg[i] = *(const u32x4*)(kh + (size_t)key * D + cch * 8);
+      vreg[i] = *(const u32x4*)(vh + (size_t)key * D + cch * 8);
     }
   };
   lds_char* ks_ = smem;
@@ -117,6 +115,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   const int tr_d = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
   load_tile(k_begin);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // Q fragment and first tile landed
   for (int t0 = k_begin; t0 < k_end; t0 += kTileKeys) {
     __syncthreads();  // every wave is done with the previous tile
     store_tile();

@@ -150,23 +150,184 @@ __device__ __forceinline__ Work decode_work(const FwdArgs& a) {
 }
 
 // ------------------------------------------------------------------------
-// bf16 inputs
+// bf16 inputs.  A work-group is 4 waves = 128 query rows (32 per wave); two
+// work-groups share a CU, so each SIMD interleaves two waves.  K/V tiles of
+// 64 keys are copied global -> LDS with global_load_lds_dwordx4 (no staging
+// registers) into two stages held in separate LDS arrays, the copy of tile
+// t+1 overlapping the compute of tile t; one barrier per tile.
+//
+// LDS rows are padded instead of swizzled so that every operand read is a
+// per-lane base plus an immediate offset:
+//   K: pitch row+16 B -- the 16 rows read by a 16-lane group at one column
+//      start 4 banks apart;
+//   V: pitch row+64 B -- the 4 rows x 64 B of a transposed read start 16
+//      banks apart.
 // ------------------------------------------------------------------------
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
-  using Tile = BfTile<D>;
-  constexpr int BC = 64;
-  constexpr int TILE_BYTES = BC * Tile::kRowBytes;
-  constexpr int KS = D / 16;   // k-steps of S^T
-  constexpr int NDB = D / 32;  // 32-wide d blocks of O^T
-  constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // 16 B loads per thread per tensor per tile
-  using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
+constexpr int kBfWaves = 4;
+constexpr int kBfThreads = 64 * kBfWaves;
+constexpr int kBc = 64;  // keys per tile
+static_assert(kBfWaves * kRowsPerWave == kBr, "one 32-row block per wave");
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * 2 * TILE_BYTES];
-  lds_char* smem = (lds_char*)smem_raw;
+template <int D>
+struct BfLayout {
+  static constexpr int kRow = D * 2;           // bytes of one K/V row
+  static constexpr int kChunks = kRow / 16;    // 16 B chunks per row
+  static constexpr int kKPitch = kRow + 16;
+  static constexpr int kVPitch = kRow + 64;
+  static constexpr int kKBytes = kBc * kKPitch;
+  static constexpr int kVBytes = kBc * kVPitch;
+  static constexpr int kKPieces = kKBytes / 1024;  // 1 KB DMA pieces per tile
+  static constexpr int kVPieces = kVBytes / 1024;
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "whole DMA pieces");
+  static constexpr int kKPerWave = (kKPieces + kBfWaves - 1) / kBfWaves;
+  static constexpr int kVPerWave = (kVPieces + kBfWaves - 1) / kBfWaves;
+};
+
+// Byte offset, within a tile of the global tensor, of the 16 B that lane
+// `lane` copies for DMA piece pc of a layout with the given pitch.  Slots past
+// the row (padding) copy the row's first chunk; rows are clamped to max_row.
+template <int D>
+__device__ __forceinline__ uint32_t dma_src_off(int pc, int lane, int pitch, int max_row) {
+  using L = BfLayout<D>;
+  const int slots = pitch / 16;
+  const int slot = pc * 64 + lane;
+  int r = slot / slots, c = slot % slots;
+  if (c >= L::kChunks) c = 0;
+  r = min(r, max_row);
+  return (uint32_t)(r * L::kRow + c * 16);
+}
+
+template <int D>
+struct TileCopy {
+  using L = BfLayout<D>;
+  uint32_t koff[L::kKPerWave], voff[L::kVPerWave];  // full-tile offsets of this lane
+  int wave, lane;
+  __device__ __forceinline__ void init(int w, int l) {
+    wave = w;
+    lane = l;
+#pragma unroll
+    for (int j = 0; j < L::kKPerWave; ++j) koff[j] = dma_src_off<D>(w + j * kBfWaves, l, L::kKPitch, kBc - 1);
+#pragma unroll
+    for (int j = 0; j < L::kVPerWave; ++j) voff[j] = dma_src_off<D>(w + j * kBfWaves, l, L::kVPitch, kBc - 1);
+  }
+  // Copy K and V rows [t*64, t*64+64) of one head into the two LDS arrays.
+  __device__ __forceinline__ void issue(const uint16_t* kh, const uint16_t* vh, int t, int Lk,
+                                        lds_char* kdst, lds_char* vdst) const {
+    const char* kt = (const char*)kh + (size_t)t * kBc * L::kRow;
+    const char* vt = (const char*)vh + (size_t)t * kBc * L::kRow;
+    const bool full = t * kBc + kBc <= Lk;
+    const int max_row = Lk - 1 - t * kBc;  // rows past the last key re-read it
+#pragma unroll
+    for (int j = 0; j < L::kKPerWave; ++j) {
+      const int pc = wave + j * kBfWaves;
+      if (pc < L::kKPieces) {
+        uint32_t o = full ? koff[j] : dma_src_off<D>(pc, lane, L::kKPitch, max_row);
+        __builtin_amdgcn_global_load_lds((const void*)(kt + o), kdst + pc * 1024, 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < L::kVPerWave; ++j) {
+      const int pc = wave + j * kBfWaves;
+      if (pc < L::kVPieces) {
+        uint32_t o = full ? voff[j] : dma_src_off<D>(pc, lane, L::kVPitch, max_row);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + o), vdst + pc * 1024, 16, 0, 0);
+      }
+    }
+  }
+};
+
+// One 64-key tile for the wave's 32 rows: S^T = K Q^T, mask, online softmax,
+// O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* vs_, int kbase,
+                                          int vbase, const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
+                                          Row& row, int kind, int t0, int vis_lo, int vis_hi,
+                                          int half, float c) {
+  using L = BfLayout<D>;
+  f32x16 st[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    st[kb] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8 kf = as_bf16x8(lds_read16(ks_, kbase + kb * 32 * L::kKPitch + ks * 32));
+      st[kb] = mfma_32x32x16(kf, qf[ks], st[kb]);
+    }
+  }
+  float s[32];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[kb * 16 + v] = st[kb][v];
+  if (kind == 2) {
+    const int lo = vis_lo - t0, hi = vis_hi - t0;  // visible offsets within the tile
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        int j = kb * 32 + key_of_reg(v, half);
+        s[kb * 16 + v] = (j >= lo && j <= hi) ? s[kb * 16 + v] : kNegInf;
+      }
+  }
+  float alpha = softmax_tile<32>(s, row, c);
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+  }
+  bf16x8 pf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const float* x = s + kb * 16 + s2 * 8;
+      pf[kb][s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int off = vbase + (kb * 32 + s2 * 16) * L::kVPitch + db * 64;
+        i16x4 lo = lds_read_tr16(vs_, off);
+        i16x4 hi = lds_read_tr16(vs_, off + 4 * L::kVPitch);
+        o[db] = mfma_32x32x16(join_tr(lo, hi), pf[kb][s2], o[db]);
+      }
+}
+
+template <int D>
+struct BfSmem {
+  using L = BfLayout<D>;
+  static __device__ __forceinline__ lds_char* k0() {
+    __shared__ __attribute__((aligned(1024))) char buf[L::kKBytes];
+    return (lds_char*)buf;
+  }
+  static __device__ __forceinline__ lds_char* k1() {
+    __shared__ __attribute__((aligned(1024))) char buf[L::kKBytes];
+    return (lds_char*)buf;
+  }
+  static __device__ __forceinline__ lds_char* v0() {
+    __shared__ __attribute__((aligned(1024))) char buf[L::kVBytes];
+    return (lds_char*)buf;
+  }
+  static __device__ __forceinline__ lds_char* v1() {
+    __shared__ __attribute__((aligned(1024))) char buf[L::kVBytes];
+    return (lds_char*)buf;
+  }
+};
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+  using L = BfLayout<D>;
+  using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
+  lds_char* K0 = BfSmem<D>::k0();
+  lds_char* K1 = BfSmem<D>::k1();
+  lds_char* V0 = BfSmem<D>::v0();
+  lds_char* V1 = BfSmem<D>::v1();
 
   const Work wk = decode_work(a);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int off_q = a.Lk - a.Lq;
 
@@ -174,154 +335,65 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const uint16_t* kh = (const uint16_t*)a.k + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
   const uint16_t* vh = (const uint16_t*)a.v + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
 
-  // Rows of the work-group and of this wave.
   const int r0 = wk.qt * kBr;
   const int r_end = min(r0 + kBr, a.Lq);
-  RowSpan wg_span = {r0 + off_q, r_end - 1 + off_q};
+  const RowSpan wg_span = {r0 + off_q, r_end - 1 + off_q};
   const int w0 = r0 + wave * kRowsPerWave;
   const bool wave_active = w0 < a.Lq;
-  RowSpan w_span = {w0 + off_q, min(w0 + kRowsPerWave, a.Lq) - 1 + off_q};
+  const RowSpan w_span = {w0 + off_q, min(w0 + kRowsPerWave, a.Lq) - 1 + off_q};
+  const int key_lo = a.window > 0 ? max(0, wg_span.p_first - a.window + 1) : 0;
+  const int key_hi = wg_span.p_last + 1;
+  const int t_begin = key_lo / kBc, t_end = (key_hi + kBc - 1) / kBc;
 
-  // Key tiles the work-group needs.
-  int key_lo = a.window > 0 ? max(0, wg_span.p_first - a.window + 1) : 0;
-  int key_hi = wg_span.p_last + 1;
-  const int t_begin = key_lo / BC, t_end = (key_hi + BC - 1) / BC;
+  TileCopy<D> cp;
+  cp.init(wave, lane);
+  cp.issue(kh, vh, t_begin, a.Lk, K0, V0);
 
   // Q^T operand: lane holds query row w0+col, d = ks*16 + half*8 .. +8.
   const int my_row = w0 + col;
   const bool row_valid = my_row < a.Lq;
-  bf16x8 qf[KS];
+  bf16x8 qf[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < D / 16; ++ks) {
     u32x4 v = {0, 0, 0, 0};
     if (row_valid) v = *(const u32x4*)(qh + (size_t)my_row * D + ks * 16 + half * 8);
     qf[ks] = as_bf16x8(v);
   }
-
-  f32x16 o[NDB];
+  f32x16 o[D / 32];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
+  for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
   Row row = {kNegInf, 0.0f};
-
-  // Mask bounds of this lane's row: visible keys are [vis_lo, vis_hi].
   const int p = my_row + off_q;
   const int vis_hi = min(p, a.Lk - 1);
   const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
 
-  // Staging: thread t moves 16 B chunks t + i*kThreads of each tile.
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int cid = threadIdx.x + i * kThreads;
-      int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
-      int key = t * BC + r;
-      if (key < a.Lk) {
-        kreg[i] = *(const u32x4*)(kh + (size_t)key * D + cch * 8);
-        vreg[i] = *(const u32x4*)(vh + (size_t)key * D + cch * 8);
-      } else {
-        kreg[i] = (u32x4){0, 0, 0, 0};
-        vreg[i] = (u32x4){0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    lds_char* ks_ = smem + buf * 2 * TILE_BYTES;
-    lds_char* vs_ = ks_ + TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int cid = threadIdx.x + i * kThreads;
-      int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
-      int off = Tile::off(r, cch * 16);
-      lds_write16(ks_, off, kreg[i]);
-      lds_write16(vs_, off, vreg[i]);
-    }
+  // Per-lane operand read bases (see bf16_tile for the immediates).
+  const int kbase = key_perm(col) * L::kKPitch + half * 16;
+  const int vbase = (half * 8 + ((lane & 15) >> 2)) * L::kVPitch +
+                    (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
+
+  auto step = [&](int t, const lds_char* ks_, const lds_char* vs_) {
+    const int kind = wave_active ? tile_kind(t * kBc, kBc, w_span, a.window, a.Lk) : 0;
+    if (kind != 0)
+      bf16_tile<D>(ks_, vs_, kbase, vbase, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
   };
 
-  // Per-lane constant parts of the LDS addresses.
-  // K operand: row kb*32 + key_perm(col), bytes (ks*2 + half)*16.
-  const int k_row = key_perm(col);
-  // V^T operand via transposed reads: lane j of each 16-lane group addresses
-  // key (base + j/4), d = db*32 + ((lane/16)%2)*16 + (j%4)*4.
-  const int tr_key = (lane & 15) >> 2;
-  const int tr_d = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    if (more) load_tile(t + 1);
-
-    const int t0 = t * BC;
-    const int kind = wave_active ? tile_kind(t0, BC, w_span, a.window, a.Lk) : 0;
-    if (kind != 0) {
-      const lds_char* ks_ = smem + buf * 2 * TILE_BYTES;
-      const lds_char* vs_ = ks_ + TILE_BYTES;
-      f32x16 st[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = (f32x16){};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8 kf = as_bf16x8(lds_read16(ks_, Tile::off(kb * 32 + k_row, (ks * 2 + half) * 16)));
-          st[kb] = mfma_32x32x16(kf, qf[ks], st[kb]);
-        }
-      }
-      float s[32];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[kb * 16 + v] = st[kb][v];
-      if (kind == 2) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            int j = t0 + kb * 32 + key_of_reg(v, half);
-            bool vis = (j >= vis_lo) & (j <= vis_hi);
-            s[kb * 16 + v] = vis ? s[kb * 16 + v] : kNegInf;
-          }
-      }
-      float alpha = softmax_tile<32>(s, row, a.c);
-      if (alpha != 1.0f) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const float* x = s + kb * 16 + s2 * 8;
-          pf[kb][s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
-        }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            int key = kb * 32 + s2 * 16 + half * 8 + tr_key;
-            int dd = db * 32 + tr_d;
-            i16x4 lo = lds_read_tr16(vs_, Tile::off(key, dd * 2));
-            i16x4 hi = lds_read_tr16(vs_, Tile::off(key + 4, dd * 2));
-            o[db] = mfma_32x32x16(join_tr(lo, hi), pf[kb][s2], o[db]);
-          }
-      }
-    }
-    if (more) store_tile(buf ^ 1);
+  for (int t = t_begin; t < t_end; t += 2) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // tile t is in K0/V0 (this wave's copies)
+    __syncthreads();                          // ... and everyone's; K1/V1 are free
+    if (t + 1 < t_end) cp.issue(kh, vh, t + 1, a.Lk, K1, V1);
+    step(t, K0, V0);
+    if (t + 1 >= t_end) break;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    if (t + 2 < t_end) cp.issue(kh, vh, t + 2, a.Lk, K0, V0);
+    step(t + 1, K1, V1);
   }
 
   const float sink_l2 = a.sinks ? a.sinks[wk.h] * kLog2e : kNegInf;
   OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row) * D;
   float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row : nullptr;
-  finalize_store<NDB, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
+  finalize_store<D / 32, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
 }
 
 // ------------------------------------------------------------------------
@@ -340,7 +412,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   __shared__ float smem[2][TILE_FLOATS];  // [K/V]; single buffer, registers prefetch
 
   const Work wk = decode_work(a);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int off_q = a.Lk - a.Lq;
 
@@ -378,14 +451,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
     for (int i = 0; i < LOADS; ++i) {
       int cid = threadIdx.x + i * kThreads;
       int r = cid / (D / 4), c4 = cid % (D / 4);
-      int key = t * BC + r;
-      if (key < a.Lk) {
-        kreg[i] = *(const f32x4*)(kh + (size_t)key * D + c4 * 4);
-        vreg[i] = *(const f32x4*)(vh + (size_t)key * D + c4 * 4);
-      } else {
-        kreg[i] = (f32x4){0, 0, 0, 0};
-        vreg[i] = (f32x4){0, 0, 0, 0};
-      }
+      int key = min(t * BC + r, a.Lk - 1);
+      kreg[i] = *(const f32x4*)(kh + (size_t)key * D + c4 * 4);
+      vreg[i] = *(const f32x4*)(vh + (size_t)key * D + c4 * 4);
     }
   };
   auto store_tile = [&]() {
@@ -450,9 +518,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
 }
 
 template <typename K>
-hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream) {
+hipError_t launch(K kernel, int threads, const FwdArgs& a, hipStream_t stream) {
   int total = a.n_qtiles * a.Hq * a.B;
-  hipLaunchKernelGGL(kernel, dim3(total), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(total), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -467,15 +535,17 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
   a.c = scale * kLog2e;
   a.n_qtiles = (Lq + kBr - 1) / kBr;
   if (!in_f32) {
-    if (D == 128) return out_f32 ? launch(fwd_bf16_kernel<128, true>, a, stream)
-                                 : launch(fwd_bf16_kernel<128, false>, a, stream);
-    return out_f32 ? launch(fwd_bf16_kernel<64, true>, a, stream)
-                   : launch(fwd_bf16_kernel<64, false>, a, stream);
+    const int t = kBfThreads;
+    if (D == 128) return out_f32 ? launch(fwd_bf16_kernel<128, true>, t, a, stream)
+                                 : launch(fwd_bf16_kernel<128, false>, t, a, stream);
+    return out_f32 ? launch(fwd_bf16_kernel<64, true>, t, a, stream)
+                   : launch(fwd_bf16_kernel<64, false>, t, a, stream);
   }
-  if (D == 128) return out_f32 ? launch(fwd_f32_kernel<128, true>, a, stream)
-                               : launch(fwd_f32_kernel<128, false>, a, stream);
-  return out_f32 ? launch(fwd_f32_kernel<64, true>, a, stream)
-                 : launch(fwd_f32_kernel<64, false>, a, stream);
+  const int t = kThreads;
+  if (D == 128) return out_f32 ? launch(fwd_f32_kernel<128, true>, t, a, stream)
+                               : launch(fwd_f32_kernel<128, false>, t, a, stream);
+  return out_f32 ? launch(fwd_f32_kernel<64, true>, t, a, stream)
+                 : launch(fwd_f32_kernel<64, false>, t, a, stream);
 }
 
 int fwd_grid_size(int B, int Hq, int Lq) { return ((Lq + kBr - 1) / kBr) * Hq * B; }
