@@ -36,7 +36,7 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, int 
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0 || Lq > Lk) return ATTN_ERR_SHAPE;
   if (!fits(B, Hq, Lq, D) || !fits(B, Hkv, Lk, D)) return ATTN_ERR_SHAPE;
-  // grid: one work-group per 128 query rows of each (batch, head)
+  // grid: one work-group per 128 (fp32) or 256 (bf16) query rows of each (batch, head)
   if ((long long)((Lq + 127) / 128) * Hq * B >= (1LL << 31)) return ATTN_ERR_SHAPE;
   if ((long long)B * Hq >= (1LL << 31)) return ATTN_ERR_SHAPE;
   // K/V rows of one head are addressed with 32-bit byte offsets.

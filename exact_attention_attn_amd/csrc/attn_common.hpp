@@ -33,6 +33,27 @@ typedef __attribute__((address_space(3))) char lds_char;
 // (vmcnt = 0) and leaves the export and LDS counters unconstrained.
 constexpr int kWaitVmcnt0 = (7 << 4) | (0xF << 8);
 
+// s_waitcnt immediate for vmcnt <= n (0 <= n < 64), other counters unconstrained.
+__host__ __device__ constexpr int wait_vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8);
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding; n is
+// wave-uniform.  Counts the switch does not list fall back to waiting for all.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(8)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0)); break;
+  }
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -150,11 +150,15 @@ __device__ __forceinline__ Work decode_work(const FwdArgs& a) {
 }
 
 // ------------------------------------------------------------------------
-// bf16 inputs.  A work-group is 4 waves = 128 query rows (32 per wave); two
-// work-groups share a CU, so each SIMD interleaves two waves.  K/V tiles of
+// bf16 inputs.  A work-group is 4 waves of 32 query rows each, drawn from the
+// query heads of one KV head (4 heads x 32 rows when 4 divides the GQA group,
+// 2 x 64, or 1 x 128), so every K/V tile brought into LDS serves 4 waves while
+// the key span stays that of 32 (or 64, 128) rows.  Two work-groups per CU:
+// each SIMD interleaves two waves, and one work-group computes while the
+// other waits at its barrier.  K/V tiles of
 // 64 keys are copied global -> LDS with global_load_lds_dwordx4 (no staging
-// registers) into two stages held in separate LDS arrays, the copy of tile
-// t+1 overlapping the compute of tile t; one barrier per tile.
+// registers) into a two-stage ring of separate LDS arrays, one tile ahead of
+// its use; one barrier per tile.
 //
 // LDS rows are padded instead of swizzled so that every operand read is a
 // per-lane base plus an immediate offset:
@@ -166,7 +170,6 @@ __device__ __forceinline__ Work decode_work(const FwdArgs& a) {
 constexpr int kBfWaves = 4;
 constexpr int kBfThreads = 64 * kBfWaves;
 constexpr int kBc = 64;  // keys per tile
-static_assert(kBfWaves * kRowsPerWave == kBr, "one 32-row block per wave");
 
 template <int D>
 struct BfLayout {
@@ -202,9 +205,11 @@ struct TileCopy {
   using L = BfLayout<D>;
   uint32_t koff[L::kKPerWave], voff[L::kVPerWave];  // full-tile offsets of this lane
   int wave, lane;
+  int count;  // copies this wave issues per tile
   __device__ __forceinline__ void init(int w, int l) {
     wave = w;
     lane = l;
+    count = (L::kKPieces - w + kBfWaves - 1) / kBfWaves + (L::kVPieces - w + kBfWaves - 1) / kBfWaves;
 #pragma unroll
     for (int j = 0; j < L::kKPerWave; ++j) koff[j] = dma_src_off<D>(w + j * kBfWaves, l, L::kKPitch, kBc - 1);
 #pragma unroll
@@ -236,43 +241,70 @@ struct TileCopy {
   }
 };
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+
 // One 64-key tile for the wave's 32 rows: S^T = K Q^T, mask, online softmax,
-// O^T += V^T P^T.
+// O^T += V^T P^T.  Operand reads run ahead of the MFMAs that consume them
+// (the two S^T accumulators and the D/32 O^T accumulators are independent
+// chains, so consecutive MFMAs never wait on each other).
 template <int D>
 __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* vs_, int kbase,
                                           int vbase, const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                           Row& row, int kind, int t0, int vis_lo, int vis_hi,
                                           int half, float c) {
   using L = BfLayout<D>;
-  f32x16 st[2];
+  constexpr int KS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int KA = 4;  // K k-steps read ahead (both key blocks)
+
+  // S^T for key blocks 0 and 1, k-steps interleaved.
+  f32x16 st0 = (f32x16){}, st1 = (f32x16){};
+  bf16x8 k0[KS], k1[KS];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    st[kb] = (f32x16){};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8 kf = as_bf16x8(lds_read16(ks_, kbase + kb * 32 * L::kKPitch + ks * 32));
-      st[kb] = mfma_32x32x16(kf, qf[ks], st[kb]);
-    }
+  for (int ks = 0; ks < KA; ++ks) {
+    k0[ks] = as_bf16x8(lds_read16(ks_, kbase + ks * 32));
+    k1[ks] = as_bf16x8(lds_read16(ks_, kbase + 32 * L::kKPitch + ks * 32));
   }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + KA < KS) {
+      k0[ks + KA] = as_bf16x8(lds_read16(ks_, kbase + (ks + KA) * 32));
+      k1[ks + KA] = as_bf16x8(lds_read16(ks_, kbase + 32 * L::kKPitch + (ks + KA) * 32));
+    }
+    st0 = mfma_32x32x16(k0[ks], qf[ks], st0);
+    st1 = mfma_32x32x16(k1[ks], qf[ks], st1);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * KA, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + KA < KS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+  }
+
   float s[32];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[kb * 16 + v] = st[kb][v];
+  for (int v = 0; v < 16; ++v) {
+    s[v] = st0[v];
+    s[16 + v] = st1[v];
+  }
   if (kind == 2) {
-    const int lo = vis_lo - t0, hi = vis_hi - t0;  // visible offsets within the tile
+    // keep key offset j iff lo <= j <= hi, as one unsigned compare
+    const unsigned lo = (unsigned)(vis_lo - t0);
+    const unsigned span = (unsigned)(vis_hi - vis_lo);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        int j = kb * 32 + key_of_reg(v, half);
-        s[kb * 16 + v] = (j >= lo && j <= hi) ? s[kb * 16 + v] : kNegInf;
+        const unsigned j = (unsigned)(kb * 32 + key_of_reg(v, half));
+        s[kb * 16 + v] = (j - lo <= span) ? s[kb * 16 + v] : kNegInf;
       }
   }
   float alpha = softmax_tile<32>(s, row, c);
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
   }
   bf16x8 pf[2][2];
 #pragma unroll
@@ -282,69 +314,106 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
       const float* x = s + kb * 16 + s2 * 8;
       pf[kb][s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
+
+  // O^T += V^T P^T: step (kb, s2) feeds the D/32 independent accumulators.
+  constexpr int NSTEP = 4 * NDB;  // (kb, s2, db) triples
+  constexpr int VA = NDB;         // V operands read ahead
+  bf16x8 vf[NSTEP];
+  auto vread = [&](int i) {
+    const int db = i % NDB, ks2 = i / NDB;  // ks2 = kb*2 + s2
+    const int off = vbase + ks2 * 16 * L::kVPitch + db * 64;
+    vf[i] = join_tr(lds_read_tr16(vs_, off), lds_read_tr16(vs_, off + 4 * L::kVPitch));
+  };
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int i = 0; i < VA; ++i) vread(i);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int i = 0; i < NSTEP; ++i) {
+    if (i + VA < NSTEP) vread(i + VA);
+    const int db = i % NDB, ks2 = i / NDB;
+    o[db] = mfma_32x32x16(vf[i], pf[ks2 >> 1][ks2 & 1], o[db]);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * VA, 1);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int off = vbase + (kb * 32 + s2 * 16) * L::kVPitch + db * 64;
-        i16x4 lo = lds_read_tr16(vs_, off);
-        i16x4 hi = lds_read_tr16(vs_, off + 4 * L::kVPitch);
-        o[db] = mfma_32x32x16(join_tr(lo, hi), pf[kb][s2], o[db]);
-      }
+  for (int i = 0; i < NSTEP; ++i) {
+    if (i + VA < NSTEP) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
+  }
 }
 
 template <int D>
 struct BfSmem {
   using L = BfLayout<D>;
-  static __device__ __forceinline__ lds_char* k0() {
+  template <int I>
+  static __device__ __forceinline__ lds_char* k() {
     __shared__ __attribute__((aligned(1024))) char buf[L::kKBytes];
     return (lds_char*)buf;
   }
-  static __device__ __forceinline__ lds_char* k1() {
-    __shared__ __attribute__((aligned(1024))) char buf[L::kKBytes];
-    return (lds_char*)buf;
-  }
-  static __device__ __forceinline__ lds_char* v0() {
-    __shared__ __attribute__((aligned(1024))) char buf[L::kVBytes];
-    return (lds_char*)buf;
-  }
-  static __device__ __forceinline__ lds_char* v1() {
+  template <int I>
+  static __device__ __forceinline__ lds_char* v() {
     __shared__ __attribute__((aligned(1024))) char buf[L::kVBytes];
     return (lds_char*)buf;
   }
 };
 
+// Work of one bf16 work-group: the HG query heads hg*HG .. of KV head kvh
+// (they share every K/V tile) over the same rows [r0, r0 + rows).  Longest
+// q-tiles first within each (batch, KV head, head group).
+struct BfWork {
+  int b, kvh, hg, qt;
+};
+__device__ __forceinline__ BfWork decode_bf_work(const FwdArgs& a, int n_hg) {
+  int total = a.n_qtiles * n_hg * a.Hkv * a.B;
+  int id = xcd_remap(blockIdx.x, total);
+  BfWork w;
+  w.qt = a.n_qtiles - 1 - id % a.n_qtiles;
+  id /= a.n_qtiles;
+  w.hg = id % n_hg;
+  id /= n_hg;
+  w.kvh = id % a.Hkv;
+  w.b = id / a.Hkv;
+  return w;
+}
+
+// Query heads per work-group for a GQA group of G heads: the largest power
+// of two <= kBfWaves that divides G.
+__host__ __device__ __forceinline__ int bf_heads_per_group(int G) {
+  return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+}
+
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using L = BfLayout<D>;
   using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
-  lds_char* K0 = BfSmem<D>::k0();
-  lds_char* K1 = BfSmem<D>::k1();
-  lds_char* V0 = BfSmem<D>::v0();
-  lds_char* V1 = BfSmem<D>::v1();
+  lds_char* K0 = BfSmem<D>::template k<0>();
+  lds_char* K1 = BfSmem<D>::template k<1>();
+  lds_char* V0 = BfSmem<D>::template v<0>();
+  lds_char* V1 = BfSmem<D>::template v<1>();
 
-  const Work wk = decode_work(a);
+  const int G = a.Hq / a.Hkv;
+  const int HG = bf_heads_per_group(G);
+  const int rows = kBfWaves / HG * kRowsPerWave;  // query rows per work-group
+  const BfWork wk = decode_bf_work(a, G / HG);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int off_q = a.Lk - a.Lq;
+  const int h = wk.kvh * G + wk.hg * HG + wave % HG;  // this wave's query head
 
-  const uint16_t* qh = (const uint16_t*)a.q + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq) * D;
+  const uint16_t* qh = (const uint16_t*)a.q + ((size_t)(wk.b * a.Hq + h) * a.Lq) * D;
   const uint16_t* kh = (const uint16_t*)a.k + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
   const uint16_t* vh = (const uint16_t*)a.v + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
 
-  const int r0 = wk.qt * kBr;
-  const int r_end = min(r0 + kBr, a.Lq);
+  const int r0 = wk.qt * rows;
+  const int r_end = min(r0 + rows, a.Lq);
   const RowSpan wg_span = {r0 + off_q, r_end - 1 + off_q};
-  const int w0 = r0 + wave * kRowsPerWave;
+  const int w0 = r0 + (wave / HG) * kRowsPerWave;
   const bool wave_active = w0 < a.Lq;
   const RowSpan w_span = {w0 + off_q, min(w0 + kRowsPerWave, a.Lq) - 1 + off_q};
   const int key_lo = a.window > 0 ? max(0, wg_span.p_first - a.window + 1) : 0;
   const int key_hi = wg_span.p_last + 1;
   const int t_begin = key_lo / kBc, t_end = (key_hi + kBc - 1) / kBc;
 
+  // Two-stage ring: tile t lives in stage (t - t_begin) % 2.
   TileCopy<D> cp;
   cp.init(wave, lane);
   cp.issue(kh, vh, t_begin, a.Lk, K0, V0);
@@ -372,27 +441,25 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int vbase = (half * 8 + ((lane & 15) >> 2)) * L::kVPitch +
                     (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
 
-  auto step = [&](int t, const lds_char* ks_, const lds_char* vs_) {
+  // One ring step: wait for tile t (the only copies in flight), release the
+  // stage of tile t-1 and refill it with tile t+1, compute tile t.
+  auto step = [&](int t, const lds_char* ks_, const lds_char* vs_, lds_char* kn, lds_char* vn) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (t + 1 < t_end) cp.issue(kh, vh, t + 1, a.Lk, kn, vn);
     const int kind = wave_active ? tile_kind(t * kBc, kBc, w_span, a.window, a.Lk) : 0;
     if (kind != 0)
       bf16_tile<D>(ks_, vs_, kbase, vbase, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
   };
-
   for (int t = t_begin; t < t_end; t += 2) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // tile t is in K0/V0 (this wave's copies)
-    __syncthreads();                          // ... and everyone's; K1/V1 are free
-    if (t + 1 < t_end) cp.issue(kh, vh, t + 1, a.Lk, K1, V1);
-    step(t, K0, V0);
+    step(t, K0, V0, K1, V1);
     if (t + 1 >= t_end) break;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 2 < t_end) cp.issue(kh, vh, t + 2, a.Lk, K0, V0);
-    step(t + 1, K1, V1);
+    step(t + 1, K1, V1, K0, V0);
   }
 
-  const float sink_l2 = a.sinks ? a.sinks[wk.h] * kLog2e : kNegInf;
-  OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row) * D;
-  float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row : nullptr;
+  const float sink_l2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+  OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + h) * a.Lq + my_row) * D;
+  float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + h) * a.Lq + my_row : nullptr;
   finalize_store<D / 32, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
 }
 
@@ -518,8 +585,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
 }
 
 template <typename K>
-hipError_t launch(K kernel, int threads, const FwdArgs& a, hipStream_t stream) {
-  int total = a.n_qtiles * a.Hq * a.B;
+hipError_t launch(K kernel, int threads, const FwdArgs& a, hipStream_t stream, int heads_per_wg) {
+  int total = a.n_qtiles * (a.Hq / heads_per_wg) * a.B;
   hipLaunchKernelGGL(kernel, dim3(total), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
@@ -533,21 +600,23 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
   a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.out = out; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.window = window;
   a.c = scale * kLog2e;
-  a.n_qtiles = (Lq + kBr - 1) / kBr;
   if (!in_f32) {
+    const int HG = bf_heads_per_group(Hq / Hkv);
+    const int rows = kBfWaves / HG * kRowsPerWave;
+    a.n_qtiles = (Lq + rows - 1) / rows;
     const int t = kBfThreads;
-    if (D == 128) return out_f32 ? launch(fwd_bf16_kernel<128, true>, t, a, stream)
-                                 : launch(fwd_bf16_kernel<128, false>, t, a, stream);
-    return out_f32 ? launch(fwd_bf16_kernel<64, true>, t, a, stream)
-                   : launch(fwd_bf16_kernel<64, false>, t, a, stream);
+    if (D == 128) return out_f32 ? launch(fwd_bf16_kernel<128, true>, t, a, stream, HG)
+                                 : launch(fwd_bf16_kernel<128, false>, t, a, stream, HG);
+    return out_f32 ? launch(fwd_bf16_kernel<64, true>, t, a, stream, HG)
+                   : launch(fwd_bf16_kernel<64, false>, t, a, stream, HG);
   }
+  a.n_qtiles = (Lq + kBr - 1) / kBr;
   const int t = kThreads;
-  if (D == 128) return out_f32 ? launch(fwd_f32_kernel<128, true>, t, a, stream)
-                               : launch(fwd_f32_kernel<128, false>, t, a, stream);
-  return out_f32 ? launch(fwd_f32_kernel<64, true>, t, a, stream)
-                 : launch(fwd_f32_kernel<64, false>, t, a, stream);
+  if (D == 128) return out_f32 ? launch(fwd_f32_kernel<128, true>, t, a, stream, 1)
+                               : launch(fwd_f32_kernel<128, false>, t, a, stream, 1);
+  return out_f32 ? launch(fwd_f32_kernel<64, true>, t, a, stream, 1)
+                 : launch(fwd_f32_kernel<64, false>, t, a, stream, 1);
 }
 
-int fwd_grid_size(int B, int Hq, int Lq) { return ((Lq + kBr - 1) / kBr) * Hq * B; }
 
 }  // namespace attn
