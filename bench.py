@@ -4,7 +4,7 @@ One step = the whole path on resident synthetic inputs:
   attn_fwd            sliding-window prefill  B1 Hq64 Hkv8 L8192 D128 bf16, window 513,
                       sinks (heads h%8==0 at +20), O written in bf16
   attn_decode_splitkv split-KV decode  B64 Hq64 Hkv8 D128 bf16, Lk ~ U{1024..32768},
-                      num_splits = clamp(ceil(Lk/512), 1, 64)
+                      num_splits = clamp(ceil(Lk/1024), 1, 64)
   attn_combine        merge of the valid splits, sink added once
 
 Prints one JSON line.  `value` is the prefill's TFLOP/s (algorithmic flops:
@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="swa_prefill",
                     help="prefill workload (swa_prefill is the headline; others for study)")
+    ap.add_argument("--keys-per-split", type=int, default=0,
+                    help="decode split policy: num_splits = clamp(ceil(Lk / this), 1, 64); "
+                         "0 keeps the workload's 1024")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -137,6 +140,8 @@ def main():
     # decode inputs
     wd = W.SPLITKV_DECODE
     dq, dk, dv, seqlens, nsplits, dsinks = W.decode_inputs(wd)
+    if args.keys_per_split > 0:
+        nsplits = W.splits_policy(seqlens, args.keys_per_split)
     qd, kd, vd = up(dq, W.BF16), up(dk, W.BF16), up(dv, W.BF16)
     del dk, dv
     sl = torch.from_numpy(seqlens).to(dev)
@@ -216,6 +221,7 @@ def main():
             "prefill_flops": flops,
             "decode_bytes": dbytes,
             "decode_sum_Lk": int(np.asarray(seqlens, np.int64).sum()),
+            "decode_keys_per_split": args.keys_per_split or wd.keys_per_split,
         },
         "roofline": {
             "bound": "mfma",

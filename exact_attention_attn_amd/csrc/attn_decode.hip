@@ -1,13 +1,15 @@
 // attn_decode.hip -- split-KV decode and the valid-split LSE combine (gfx950).
 //
-// Decode: one work-group per (split, KV head, query-column group, sequence).
-// The G = Hq/Hkv query heads that share a KV head are the columns of
-// S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each K/V byte of the split is
-// read from HBM once for all of them.  Tiles of 128 keys are staged through
-// LDS (registers prefetch the next tile while the current one is computed);
-// wave w scores keys [32w, 32w+32) of every tile with its own online-softmax
-// state, and the four states are merged through LDS at the end into the
-// split's normalised partial output and its sink-free LSE.
+// Decode: the work items are the splits of every (sequence, KV head,
+// query-column group).  The G = Hq/Hkv query heads that share a KV head are
+// the columns of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each K/V byte of a
+// split is read from HBM once for all of them.  The grid is persistent: each
+// work-group streams a contiguous range of items, 128-key tiles staged
+// through LDS, with the next tile (and, at an item's end, the next item's
+// first tile and Q) prefetched into registers while the current tile is
+// computed.  Wave w scores keys [32w, 32w+32) of every tile with its own
+// online-softmax state; at the end of an item the four states are merged
+// through LDS into the split's normalised partial output and sink-free LSE.
 //
 // Combine: one wave per (sequence, query head).  Lane s holds the LSE of
 // split s; only the n_valid splits that exist are loaded (FlashMLA patch
@@ -15,6 +17,8 @@
 // splits accumulated in their order).  The sink joins as one more logit.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
+
+#include <atomic>
 
 namespace attn {
 
@@ -34,10 +38,45 @@ struct DecArgs {
   const int32_t* nsplits;
   float* o_part;
   float* lse_part;
-  int Hq, Hkv, Lk_max, max_splits, window, n_qgroups;
+  int B, Hq, Hkv, Lk_max, max_splits, window, n_qgroups;
   float c;  // scale * log2(e)
 };
 
+// A work item: one split of one (sequence, KV head, query-column group).
+struct Item {
+  int b, kvh, qg, s, k_begin, k_end;
+};
+
+// Items of sequence b are ordered (kvh, qg, s) with s fastest, so that a run
+// of consecutive items streams consecutive cache rows.
+__device__ __forceinline__ int items_of(const DecArgs& a, int b, SplitRange& sr) {
+  sr = split_rule(a.seqlens[b], a.nsplits[b], a.Lk_max, a.max_splits, a.window);
+  return sr.n_valid * a.Hkv * a.n_qgroups;
+}
+__device__ __forceinline__ Item make_item(const DecArgs& a, int b, int r, const SplitRange& sr) {
+  Item it;
+  it.b = b;
+  it.s = r % sr.n_valid;
+  const int rest = r / sr.n_valid;
+  it.qg = rest % a.n_qgroups;
+  it.kvh = rest / a.n_qgroups;
+  it.k_begin = sr.lo + it.s * sr.chunk;
+  it.k_end = min(it.k_begin + sr.chunk, sr.Lk);
+  return it;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Persistent split-KV decode: work-group w of n streams items
+// [total*w/n, total*(w+1)/n) of the flat item list; the copy of the next tile
+// (possibly the next item's first) is in flight while a tile is computed.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   using Tile = BfTile<D>;
@@ -45,60 +84,88 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int LOADS = TILE_BYTES / 16 / kThreads;
-  constexpr int MQ = 8;           // query columns merged per pass
+  constexpr int MQ = 4;           // query columns merged per pass
   constexpr int OPITCH = D + 4;   // floats per merged row in LDS
-  static_assert(kWaves * MQ * OPITCH * 4 + 2 * kWaves * MQ * 4 <= 2 * TILE_BYTES, "merge fits");
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * TILE_BYTES];
-  lds_char* smem = (lds_char*)smem_raw;
-
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y % a.Hkv, qg = blockIdx.y / a.Hkv;
-  const int b = blockIdx.z;
-  const SplitRange sr = split_rule(a.seqlens[b], a.nsplits[b], a.Lk_max, a.max_splits, a.window);
-  if (s >= sr.n_valid) return;  // uniform over the work-group
-  const int k_begin = sr.lo + s * sr.chunk;
-  const int k_end = min(k_begin + sr.chunk, sr.Lk);
+  __shared__ __attribute__((aligned(16))) char tile_raw[2 * TILE_BYTES];
+  __shared__ float sm_o[kWaves * MQ * OPITCH];
+  __shared__ float sm_m[kWaves * MQ], sm_l[kWaves * MQ];
+  lds_char* ks_ = (lds_char*)tile_raw;
+  lds_char* vs_ = ks_ + TILE_BYTES;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int G = a.Hq / a.Hkv;
-  const int qcol = qg * 32 + col;  // query head within the group
-  const bool col_valid = qcol < G;
-  const int h = kvh * G + qcol;
 
-  const uint16_t* kh = a.k + ((size_t)(b * a.Hkv + kvh) * a.Lk_max) * D;
-  const uint16_t* vh = a.v + ((size_t)(b * a.Hkv + kvh) * a.Lk_max) * D;
-
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 v = {0, 0, 0, 0};
-    if (col_valid) v = *(const u32x4*)(a.q + ((size_t)(b * a.Hq + h)) * D + ks * 16 + half * 8);
-    qf[ks] = as_bf16x8(v);
+  // Total items and this work-group's range (every wave computes the same).
+  long long total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    SplitRange sr;
+    int n = (b0 + lane < a.B) ? items_of(a, b0 + lane, sr) : 0;
+    total += __builtin_amdgcn_readfirstlane(__shfl(wave_incl_scan(n, lane), 63));
   }
+  const long long lo = total * blockIdx.x / gridDim.x;
+  const long long hi = total * (blockIdx.x + 1) / gridDim.x;
+  if (lo >= hi) return;  // uniform over the work-group
+  int items_left = (int)(hi - lo);
 
-  f32x16 o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
-  float m_run = kNegInf, l_run = 0.0f;
+  // Locate the first item: sequence b and index r within it.
+  int cur_b = 0, cur_r = 0;
+  {
+    long long base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      SplitRange sr;
+      int n = (b0 + lane < a.B) ? items_of(a, b0 + lane, sr) : 0;
+      int incl = wave_incl_scan(n, lane);
+      long long chunk = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+      if (base + chunk > lo) {
+        // first lane whose inclusive prefix passes lo
+        unsigned long long m = __builtin_amdgcn_ballot_w64(base + incl > lo);
+        int l0 = __builtin_ctzll(m);
+        int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - n, l0));
+        cur_b = b0 + l0;
+        cur_r = (int)(lo - base - excl);
+        break;
+      }
+      base += chunk;
+    }
+  }
+  SplitRange cur_sr;
+  int cur_n = items_of(a, cur_b, cur_sr);
+  Item it = make_item(a, cur_b, cur_r, cur_sr);
 
+  // Advance to the next item (skipping sequences without keys).
+  auto advance = [&]() {
+    if (++cur_r >= cur_n) {
+      cur_r = 0;
+      do {  // a later sequence with items exists: items_left counts them
+        ++cur_b;
+        cur_n = cur_b < a.B ? items_of(a, cur_b, cur_sr) : 1;
+      } while (cur_n == 0);
+    }
+    return make_item(a, cur_b, cur_r, cur_sr);
+  };
+
+  auto kv_base = [&](const Item& x, const uint16_t* p) {
+    return p + ((size_t)(x.b * a.Hkv + x.kvh) * a.Lk_max) * D;
+  };
   u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int t0) {
+  auto load_tile = [&](const Item& x, int t0) {
+    const uint16_t* kh = kv_base(x, a.k);
+    const uint16_t* vh = kv_base(x, a.v);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       int cid = threadIdx.x + i * kThreads;
       int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
       // Rows past the split are loaded from its last key: they are masked
       // (p = 0) and finite, so they add nothing.  Rows >= Lk are never read.
-      int key = min(t0 + r, k_end - 1);
-      kreg[i] = *(const u32x4*)(kh + (size_t)key * D + cch * 8);
-      vreg[i] = *(const u32x4*)(vh + (size_t)key * D + cch * 8);
+      // Each cache byte is read once: non-temporal loads keep it out of the caches.
+      int key = min(t0 + r, x.k_end - 1);
+      kreg[i] = __builtin_nontemporal_load((const u32x4*)(kh + (size_t)key * D + cch * 8));
+      vreg[i] = __builtin_nontemporal_load((const u32x4*)(vh + (size_t)key * D + cch * 8));
     }
   };
-  lds_char* ks_ = smem;
-  lds_char* vs_ = smem + TILE_BYTES;
   auto store_tile = [&]() {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -109,33 +176,72 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
       lds_write16(vs_, off, vreg[i]);
     }
   };
+  bf16x8 qf[KS];  // Q^T operand of the current item
+  auto load_q = [&](const Item& x) {
+    const int qcol = x.qg * 32 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0, 0, 0, 0};
+      if (qcol < G) {
+        const int h = x.kvh * G + qcol;
+        v = *(const u32x4*)(a.q + ((size_t)(x.b * a.Hq + h)) * D + ks * 16 + half * 8);
+      }
+      qf[ks] = as_bf16x8(v);
+    }
+  };
 
   const int k_row = wave * kKeysPerWave + key_perm(col);
   const int tr_key = (lane & 15) >> 2;
   const int tr_d = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
-  load_tile(k_begin);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // Q fragment and first tile landed
-  for (int t0 = k_begin; t0 < k_end; t0 += kTileKeys) {
+  f32x16 o[NDB];
+  float m_run = kNegInf, l_run = 0.0f;
+
+  int t0 = it.k_begin;
+  load_q(it);
+  load_tile(it, t0);
+  while (true) {
     __syncthreads();  // every wave is done with the previous tile
     store_tile();
-    if (t0 + kTileKeys < k_end) load_tile(t0 + kTileKeys);
+    if (t0 == it.k_begin) {  // a new item starts (its Q is in qf already)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
+      m_run = kNegInf;
+      l_run = 0.0f;
+    }
+    // Prefetch the next tile: of this item, or the first of the next item.
+    const bool last = t0 + kTileKeys >= it.k_end;
+    Item nx = it;
+    int nt0 = t0 + kTileKeys;
+    const bool has_next = !last || items_left > 1;
+    if (last && has_next) {
+      nx = advance();
+      nt0 = nx.k_begin;
+    }
+    if (has_next) load_tile(nx, nt0);
     __syncthreads();
+
     const int w0 = t0 + wave * kKeysPerWave;
-    if (w0 < k_end) {
-      f32x16 st = (f32x16){};
+    const bool active = w0 < it.k_end;
+    f32x16 st = (f32x16){};
+    if (active) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         bf16x8 kf = as_bf16x8(lds_read16(ks_, Tile::off(k_row, (ks * 2 + half) * 16)));
         st = mfma_32x32x16(kf, qf[ks], st);
       }
+    }
+    // Q of the next item: qf is free once the scores of the item's last tile
+    // are issued, and the load overlaps the rest of this tile and the merge.
+    if (last && has_next) load_q(nx);
+    if (active) {
       float sv[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) sv[v] = st[v];
-      if (w0 + kKeysPerWave > k_end) {
+      if (w0 + kKeysPerWave > it.k_end) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          sv[v] = (w0 + key_of_reg(v, half) < k_end) ? sv[v] : kNegInf;
+          sv[v] = (w0 + key_of_reg(v, half) < it.k_end) ? sv[v] : kNegInf;
       }
       float mx = sv[0];
 #pragma unroll
@@ -170,54 +276,58 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
         for (int s2 = 0; s2 < 2; ++s2) {
           int key = wave * kKeysPerWave + s2 * 16 + half * 8 + tr_key;
           int dd = db * 32 + tr_d;
-          i16x4 lo = lds_read_tr16(vs_, Tile::off(key, dd * 2));
-          i16x4 hi = lds_read_tr16(vs_, Tile::off(key + 4, dd * 2));
-          o[db] = mfma_32x32x16(join_tr(lo, hi), pf[s2], o[db]);
+          i16x4 lo4 = lds_read_tr16(vs_, Tile::off(key, dd * 2));
+          i16x4 hi4 = lds_read_tr16(vs_, Tile::off(key + 4, dd * 2));
+          o[db] = mfma_32x32x16(join_tr(lo4, hi4), pf[s2], o[db]);
         }
     }
-  }
 
-  // Merge the four per-wave states of each query column through LDS.
-  const float l_tot = pair_sum(l_run);
-  float* sm_o = (float*)smem_raw;                   // [wave][MQ][OPITCH]
-  float* sm_m = sm_o + kWaves * MQ * OPITCH;        // [wave][MQ]
-  float* sm_l = sm_m + kWaves * MQ;                 // [wave][MQ]
-  const int n_cols = min(32, G - qg * 32);
-  for (int c0 = 0; c0 < n_cols; c0 += MQ) {
-    __syncthreads();
-    if (col >= c0 && col < c0 + MQ && col < n_cols) {
-      int cq = col - c0;
+    if (last) {
+      // Merge the four per-wave states of each query column into the split's
+      // normalised partial output and its sink-free LSE.
+      const float l_tot = pair_sum(l_run);
+      const int n_cols = min(32, G - it.qg * 32);
+      for (int c0 = 0; c0 < n_cols; c0 += MQ) {
+        __syncthreads();
+        if (col >= c0 && col < c0 + MQ && col < n_cols) {
+          const int cq = col - c0;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int d = db * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          sm_o[(wave * MQ + cq) * OPITCH + d] = o[db][r];
+            for (int r = 0; r < 16; ++r) {
+              int d = db * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+              sm_o[(wave * MQ + cq) * OPITCH + d] = o[db][r];
+            }
+          if (half == 0) {
+            sm_m[wave * MQ + cq] = m_run;
+            sm_l[wave * MQ + cq] = l_tot;
+          }
         }
-      if (half == 0) {
-        sm_m[wave * MQ + cq] = m_run;
-        sm_l[wave * MQ + cq] = l_tot;
-      }
-    }
-    __syncthreads();
-    const int ncq = min(MQ, n_cols - c0);
-    for (int idx = threadIdx.x; idx < ncq * D; idx += kThreads) {
-      int cq = idx / D, d = idx % D;
-      float M = kNegInf;
+        __syncthreads();
+        const int ncq = min(MQ, n_cols - c0);
+        for (int idx = threadIdx.x; idx < ncq * D; idx += kThreads) {
+          const int cq = idx / D, d = idx % D;
+          float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * MQ + cq]);
-      float L = 0.0f, acc = 0.0f;
+          for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * MQ + cq]);
+          float L = 0.0f, acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        float f = exp2_fast(sm_m[w * MQ + cq] - M);  // -inf (wave saw no key) -> 0
-        L += sm_l[w * MQ + cq] * f;
-        acc += sm_o[(w * MQ + cq) * OPITCH + d] * f;
+          for (int w = 0; w < kWaves; ++w) {
+            float f = exp2_fast(sm_m[w * MQ + cq] - M);  // -inf (wave saw no key) -> 0
+            L += sm_l[w * MQ + cq] * f;
+            acc += sm_o[(w * MQ + cq) * OPITCH + d] * f;
+          }
+          const int hh = it.kvh * G + it.qg * 32 + c0 + cq;
+          const size_t base = ((size_t)(it.b * a.Hq + hh) * a.max_splits + it.s);
+          a.o_part[base * D + d] = acc / L;
+          if (d == 0) a.lse_part[base] = (M + log2_fast(L)) * kLn2;
+        }
       }
-      int hh = kvh * G + qg * 32 + c0 + cq;
-      size_t base = ((size_t)(b * a.Hq + hh) * a.max_splits + s);
-      a.o_part[base * D + d] = acc / L;
-      if (d == 0) a.lse_part[base] = (M + log2_fast(L)) * kLn2;
+      --items_left;
     }
+    if (!has_next) break;
+    it = nx;
+    t0 = nt0;
   }
 }
 
@@ -294,6 +404,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombArgs a) {
 
 }  // namespace
 
+// Compute units of the current device, read once per device.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
                          float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
@@ -301,11 +425,13 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
   DecArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k_cache; a.v = (const uint16_t*)v_cache;
   a.seqlens = seqlens_k; a.nsplits = num_splits; a.o_part = o_part; a.lse_part = lse_part;
-  a.Hq = Hq; a.Hkv = Hkv; a.Lk_max = Lk_max; a.max_splits = max_splits; a.window = window;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lk_max = Lk_max; a.max_splits = max_splits; a.window = window;
   int G = Hq / Hkv;
   a.n_qgroups = (G + 31) / 32;
   a.c = scale * kLog2e;
-  dim3 grid(max_splits, Hkv * a.n_qgroups, B);
+  // Persistent grid: two work-groups per compute unit, each streaming a
+  // contiguous range of the item list.
+  dim3 grid(2 * cu_count());
   if (D == 128)
     hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kThreads), 0, stream, a);
   else

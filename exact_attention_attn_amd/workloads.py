@@ -15,7 +15,7 @@ swa_prefill           B1 Hq64 Hkv8 L8192 D128 bf16, window 513, sinks N(0, 2),
                       heads h % 8 == 0 forced to +20
 causal_prefill        B4 Hq32 Hkv8 L4096 D128 bf16, causal, sinks N(0, 1)
 splitkv_decode        B64 Hq64 Hkv8 Lq1 D128 bf16, Lk ~ U{1024..32768},
-                      num_splits = clamp(ceil(Lk/512), 1, 64), sinks N(0, 1),
+                      num_splits = clamp(ceil(Lk/1024), 1, 64), sinks N(0, 1),
                       cache rows >= Lk hold NaN
 long_swa_prefill      B1 Hq64 Hkv8 L262144 D128 bf16, window 513, sinks N(0, 2),
                       heads h % 4 == 0 forced to +30
@@ -106,7 +106,7 @@ class Decode:
 TINY_PREFILL = Prefill("tiny_prefill", 1, 2, 1, 256, 64, F32, 513, 1.0, 0, 0.0, 1)
 SWA_PREFILL = Prefill("swa_prefill", 1, 64, 8, 8192, 128, BF16, 513, 2.0, 8, 20.0, 2)
 CAUSAL_PREFILL = Prefill("causal_prefill", 4, 32, 8, 4096, 128, BF16, 0, 1.0, 0, 0.0, 3)
-SPLITKV_DECODE = Decode("splitkv_decode", 64, 64, 8, 1024, 32768, 128, BF16, 0, 1.0, 512, 4)
+SPLITKV_DECODE = Decode("splitkv_decode", 64, 64, 8, 1024, 32768, 128, BF16, 0, 1.0, 1024, 4)
 LONG_SWA_PREFILL = Prefill("long_swa_prefill", 1, 64, 8, 262144, 128, BF16, 513, 2.0, 4, 30.0, 5)
 
 WORKLOADS = {w.name: w for w in (TINY_PREFILL, SWA_PREFILL, CAUSAL_PREFILL, SPLITKV_DECODE,

@@ -52,7 +52,7 @@ def test_prefill_inputs_shapes_and_sinks():
 def test_decode_inputs_poison_and_splits():
     q, k, v, seqlens, ns, s = W.decode_inputs(W.SPLITKV_DECODE, B=4, Lk_max=2048)
     assert ((seqlens >= 1024) & (seqlens <= 2048)).all()
-    assert np.array_equal(ns, np.clip(-(-seqlens // 512), 1, 64))
+    assert np.array_equal(ns, np.clip(-(-seqlens // W.SPLITKV_DECODE.keys_per_split), 1, 64))
     kf = W.bf16_bits_to_f32(k)
     for b in range(4):
         assert np.isnan(kf[b, :, seqlens[b]:]).all()
