@@ -13,6 +13,10 @@ stream it runs on; decode GB/s (algorithmic bytes: the K/V rows each query
 sees plus q, O and LSE) is reported beside it.  The float64 CPU oracle is
 timed on a bounded sample of the prefill on the host cores (rank 0 only).
 
+The defaults (50 warm-up steps, about 50 ms of GPU work, then 100 timed steps)
+let the GPU reach its sustained clock before timing: the first ~20 ms of
+load after idle run measurably slower.
+
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 
@@ -22,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,14 +39,24 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank space (string literals are kept as they are)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources; stored traffic counters are used only if it matches."""
+    """Hash of the HIP sources' code (comments ignored), plus the compile flags;
+    stored traffic counters are used only while it matches."""
+    from exact_attention_attn_amd import build as B
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_attn_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(name.encode() + _code_only(f.read()).encode())
+    h.update(repr((B.DEVICE_FLAGS, sorted(B.SOURCE_FLAGS.items()))).encode())
     return h.hexdigest()[:16]
 
 
@@ -96,8 +111,8 @@ def cpu_baseline(w, q, k, v, sinks, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="swa_prefill",
                     help="prefill workload (swa_prefill is the headline; others for study)")

@@ -1,9 +1,9 @@
 // attn_fwd.hip -- fused tiled exact-attention forward for gfx950 (MI355X).
 //
-// One work-group = 4 waves = 128 query rows of one (batch, query head); each
-// wave owns 32 rows.  K/V tiles of 64 keys of the head's KV head (GQA:
-// h / (Hq/Hkv)) stream HBM -> registers -> LDS (double-buffered, one barrier
-// per tile).  Per tile and wave:
+// Each wave owns 32 query rows of one (batch, query head) and walks the K/V
+// tiles of the head's KV head (GQA: h / (Hq/Hkv)) that its rows can see; the
+// tiles are staged in LDS, double-buffered, one barrier per tile (layout and
+// copies of the bf16 path below).  Per tile and wave:
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, K from LDS, Q^T held in VGPRs;
 //                   each lane owns one query column and 32 keys of it
 //   mask            only on tiles that cut the causal diagonal, the window
@@ -17,7 +17,8 @@
 // l' = l*r + 2^(sink*log2e - m'), O = acc*r/l', LSE = ln2*(m' + log2 l').
 //
 // The float32-input variant is the same algorithm on v_mfma_f32_32x32x2_f32
-// with 32-key tiles and an fp32 LDS layout.
+// with 128-row work-groups of one head, 32-key tiles, register-staged copies
+// and an fp32 LDS layout.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -156,16 +157,18 @@ __device__ __forceinline__ Work decode_work(const FwdArgs& a) {
 // the key span stays that of 32 (or 64, 128) rows.  Two work-groups per CU:
 // each SIMD interleaves two waves, and one work-group computes while the
 // other waits at its barrier.  K/V tiles of
-// 64 keys are copied global -> LDS with global_load_lds_dwordx4 (no staging
-// registers) into a two-stage ring of separate LDS arrays, one tile ahead of
-// its use; one barrier per tile.
+// 64 keys are copied global -> LDS with buffer loads that write LDS directly
+// (no staging registers) into a two-stage ring of separate LDS arrays, one
+// tile ahead of its use; one barrier per tile.
 //
-// LDS rows are padded instead of swizzled so that every operand read is a
-// per-lane base plus an immediate offset:
-//   K: pitch row+16 B -- the 16 rows read by a 16-lane group at one column
-//      start 4 banks apart;
-//   V: pitch row+64 B -- the 4 rows x 64 B of a transposed read start 16
-//      banks apart.
+// LDS tiles use the BfTile layout (16 B chunks XOR-swizzled by row, no
+// padding), so one K or V tile is exactly 64 rows x 2D bytes and splits into
+// whole 1 KB copy pieces of 1024/(2D) rows each.  A copy instruction writes
+// its 64 x 16 B to consecutive LDS slots, so every lane fetches from global
+// memory the chunk that the swizzle stores in its slot.  Each wave issues the
+// same number of pieces per tile.  The swizzle depends only on the low four
+// bits of a row, so a lane's operand read addresses are the same for every
+// tile and for both 32-key halves of it, and are computed once.
 // ------------------------------------------------------------------------
 constexpr int kBfWaves = 4;
 constexpr int kBfThreads = 64 * kBfWaves;
@@ -173,71 +176,61 @@ constexpr int kBc = 64;  // keys per tile
 
 template <int D>
 struct BfLayout {
-  static constexpr int kRow = D * 2;           // bytes of one K/V row
-  static constexpr int kChunks = kRow / 16;    // 16 B chunks per row
-  static constexpr int kKPitch = kRow + 16;
-  static constexpr int kVPitch = kRow + 64;
-  static constexpr int kKBytes = kBc * kKPitch;
-  static constexpr int kVBytes = kBc * kVPitch;
-  static constexpr int kKPieces = kKBytes / 1024;  // 1 KB DMA pieces per tile
-  static constexpr int kVPieces = kVBytes / 1024;
-  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "whole DMA pieces");
-  static constexpr int kKPerWave = (kKPieces + kBfWaves - 1) / kBfWaves;
-  static constexpr int kVPerWave = (kVPieces + kBfWaves - 1) / kBfWaves;
+  static constexpr int kRow = D * 2;                  // bytes of one K/V row
+  static constexpr int kChunks = kRow / 16;           // 16 B chunks per row
+  static constexpr int kRowsPerPiece = 1024 / kRow;   // rows per 1 KB copy piece
+  static constexpr int kBytes = kBc * kRow;           // one K (or V) tile
+  static constexpr int kPieces = kBytes / 1024;
+  static constexpr int kPerWave = kPieces / kBfWaves;  // pieces per wave per tensor
+  static_assert(kPieces % kBfWaves == 0, "pieces split evenly over the waves");
 };
 
 // Byte offset, within a tile of the global tensor, of the 16 B that lane
-// `lane` copies for DMA piece pc of a layout with the given pitch.  Slots past
-// the row (padding) copy the row's first chunk; rows are clamped to max_row.
+// `lane` copies for piece pc: the row of the lane's slot and the chunk that
+// the swizzle stores there.
 template <int D>
-__device__ __forceinline__ uint32_t dma_src_off(int pc, int lane, int pitch, int max_row) {
+__device__ __forceinline__ uint32_t dma_src_off(int pc, int lane) {
   using L = BfLayout<D>;
-  const int slots = pitch / 16;
-  const int slot = pc * 64 + lane;
-  int r = slot / slots, c = slot % slots;
-  if (c >= L::kChunks) c = 0;
-  r = min(r, max_row);
+  const int r = pc * L::kRowsPerPiece + lane / L::kChunks;
+  const int c = (lane % L::kChunks) ^ BfTile<D>::swz(r);
   return (uint32_t)(r * L::kRow + c * 16);
 }
+
+// Word 3 of a raw (unstructured) buffer resource on CDNA: 32-bit data format,
+// no swizzle, no stride.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 template <int D>
 struct TileCopy {
   using L = BfLayout<D>;
-  uint32_t koff[L::kKPerWave], voff[L::kVPerWave];  // full-tile offsets of this lane
-  int wave, lane;
-  int count;  // copies this wave issues per tile
-  __device__ __forceinline__ void init(int w, int l) {
+  uint32_t off[L::kPerWave];  // this lane's source offsets (K and V alike)
+  int wave;
+  __device__ __forceinline__ void init(int w, int lane) {
     wave = w;
-    lane = l;
-    count = (L::kKPieces - w + kBfWaves - 1) / kBfWaves + (L::kVPieces - w + kBfWaves - 1) / kBfWaves;
 #pragma unroll
-    for (int j = 0; j < L::kKPerWave; ++j) koff[j] = dma_src_off<D>(w + j * kBfWaves, l, L::kKPitch, kBc - 1);
-#pragma unroll
-    for (int j = 0; j < L::kVPerWave; ++j) voff[j] = dma_src_off<D>(w + j * kBfWaves, l, L::kVPitch, kBc - 1);
+    for (int j = 0; j < L::kPerWave; ++j) off[j] = dma_src_off<D>(w + j * kBfWaves, lane);
   }
   // Copy K and V rows [t*64, t*64+64) of one head into the two LDS arrays.
+  // The buffer resources end at row Lk, so the rows of a last, partial tile
+  // past Lk arrive as zeros (finite, and their scores are masked).
   __device__ __forceinline__ void issue(const uint16_t* kh, const uint16_t* vh, int t, int Lk,
                                         lds_char* kdst, lds_char* vdst) const {
-    const char* kt = (const char*)kh + (size_t)t * kBc * L::kRow;
-    const char* vt = (const char*)vh + (size_t)t * kBc * L::kRow;
-    const bool full = t * kBc + kBc <= Lk;
-    const int max_row = Lk - 1 - t * kBc;  // rows past the last key re-read it
+    // The buffer-resource type exists only for the device; the host pass of
+    // this file (which only needs the kernel launch stubs) skips the body.
+#if defined(__HIP_DEVICE_COMPILE__)
+    const size_t base = (size_t)t * kBc * L::kRow;
+    const int bytes = min(kBc, Lk - t * kBc) * L::kRow;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kh + base), 0, bytes, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vh + base), 0, bytes, kRawBufferWord3);
 #pragma unroll
-    for (int j = 0; j < L::kKPerWave; ++j) {
+    for (int j = 0; j < L::kPerWave; ++j) {
       const int pc = wave + j * kBfWaves;
-      if (pc < L::kKPieces) {
-        uint32_t o = full ? koff[j] : dma_src_off<D>(pc, lane, L::kKPitch, max_row);
-        __builtin_amdgcn_global_load_lds((const void*)(kt + o), kdst + pc * 1024, 16, 0, 0);
-      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kdst + pc * 1024, 16, off[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vdst + pc * 1024, 16, off[j], 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < L::kVPerWave; ++j) {
-      const int pc = wave + j * kBfWaves;
-      if (pc < L::kVPieces) {
-        uint32_t o = full ? voff[j] : dma_src_off<D>(pc, lane, L::kVPitch, max_row);
-        __builtin_amdgcn_global_load_lds((const void*)(vt + o), vdst + pc * 1024, 16, 0, 0);
-      }
-    }
+#endif
   }
 };
 
@@ -250,8 +243,9 @@ constexpr int kSgDsRead = 0x100;
 // (the two S^T accumulators and the D/32 O^T accumulators are independent
 // chains, so consecutive MFMAs never wait on each other).
 template <int D>
-__device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* vs_, int kbase,
-                                          int vbase, const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
+__device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* vs_,
+                                          const int (&ka)[D / 16], const int (&va)[2][D / 32],
+                                          const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                           Row& row, int kind, int t0, int vis_lo, int vis_hi,
                                           int half, float c) {
   using L = BfLayout<D>;
@@ -264,14 +258,14 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
   bf16x8 k0[KS], k1[KS];
 #pragma unroll
   for (int ks = 0; ks < KA; ++ks) {
-    k0[ks] = as_bf16x8(lds_read16(ks_, kbase + ks * 32));
-    k1[ks] = as_bf16x8(lds_read16(ks_, kbase + 32 * L::kKPitch + ks * 32));
+    k0[ks] = as_bf16x8(lds_read16(ks_, ka[ks]));
+    k1[ks] = as_bf16x8(lds_read16(ks_, ka[ks] + 32 * L::kRow));
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (ks + KA < KS) {
-      k0[ks + KA] = as_bf16x8(lds_read16(ks_, kbase + (ks + KA) * 32));
-      k1[ks + KA] = as_bf16x8(lds_read16(ks_, kbase + 32 * L::kKPitch + (ks + KA) * 32));
+      k0[ks + KA] = as_bf16x8(lds_read16(ks_, ka[ks + KA]));
+      k1[ks + KA] = as_bf16x8(lds_read16(ks_, ka[ks + KA] + 32 * L::kRow));
     }
     st0 = mfma_32x32x16(k0[ks], qf[ks], st0);
     st1 = mfma_32x32x16(k1[ks], qf[ks], st1);
@@ -282,6 +276,19 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
     if (ks + KA < KS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
   }
+
+  // The first V operands of P V are read before the softmax, which hides
+  // their LDS latency behind it.
+  constexpr int NSTEP = 4 * NDB;  // (kb, s2, db) triples
+  constexpr int VA = NDB;         // V operands read ahead
+  bf16x8 vf[NSTEP];
+  auto vread = [&](int i) {
+    const int db = i % NDB, ks2 = i / NDB;  // ks2 = kb*2 + s2
+    const int rows = ks2 * 16 * L::kRow;
+    vf[i] = join_tr(lds_read_tr16(vs_, va[0][db] + rows), lds_read_tr16(vs_, va[1][db] + rows));
+  };
+#pragma unroll
+  for (int i = 0; i < VA; ++i) vread(i);
 
   float s[32];
 #pragma unroll
@@ -316,23 +323,12 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
     }
 
   // O^T += V^T P^T: step (kb, s2) feeds the D/32 independent accumulators.
-  constexpr int NSTEP = 4 * NDB;  // (kb, s2, db) triples
-  constexpr int VA = NDB;         // V operands read ahead
-  bf16x8 vf[NSTEP];
-  auto vread = [&](int i) {
-    const int db = i % NDB, ks2 = i / NDB;  // ks2 = kb*2 + s2
-    const int off = vbase + ks2 * 16 * L::kVPitch + db * 64;
-    vf[i] = join_tr(lds_read_tr16(vs_, off), lds_read_tr16(vs_, off + 4 * L::kVPitch));
-  };
-#pragma unroll
-  for (int i = 0; i < VA; ++i) vread(i);
 #pragma unroll
   for (int i = 0; i < NSTEP; ++i) {
     if (i + VA < NSTEP) vread(i + VA);
     const int db = i % NDB, ks2 = i / NDB;
     o[db] = mfma_32x32x16(vf[i], pf[ks2 >> 1][ks2 & 1], o[db]);
   }
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * VA, 1);
 #pragma unroll
   for (int i = 0; i < NSTEP; ++i) {
     if (i + VA < NSTEP) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 1);
@@ -345,12 +341,12 @@ struct BfSmem {
   using L = BfLayout<D>;
   template <int I>
   static __device__ __forceinline__ lds_char* k() {
-    __shared__ __attribute__((aligned(1024))) char buf[L::kKBytes];
+    __shared__ __attribute__((aligned(1024))) char buf[L::kBytes];
     return (lds_char*)buf;
   }
   template <int I>
   static __device__ __forceinline__ lds_char* v() {
-    __shared__ __attribute__((aligned(1024))) char buf[L::kVBytes];
+    __shared__ __attribute__((aligned(1024))) char buf[L::kBytes];
     return (lds_char*)buf;
   }
 };
@@ -436,10 +432,19 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int vis_hi = min(p, a.Lk - 1);
   const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
 
-  // Per-lane operand read bases (see bf16_tile for the immediates).
-  const int kbase = key_perm(col) * L::kKPitch + half * 16;
-  const int vbase = (half * 8 + ((lane & 15) >> 2)) * L::kVPitch +
-                    (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
+  // Per-lane operand read addresses within a stage.  K: row key_perm(col),
+  // chunk ks*2 + half.  V (transposed reads): keys half*8 + (lane%16)/4 + 4e,
+  // d = db*32 + ((lane/16)%2)*16 + (lane%4)*4.
+  using T = BfTile<D>;
+  int ka[D / 16], va[2][D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) ka[ks] = T::off(key_perm(col), (ks * 2 + half) * 16);
+  const int vrow = half * 8 + ((lane & 15) >> 2);
+  const int vbyte = (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) va[e][db] = T::off(vrow + 4 * e, db * 64 + vbyte);
 
   // One ring step: wait for tile t (the only copies in flight), release the
   // stage of tile t-1 and refill it with tile t+1, compute tile t.
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     if (t + 1 < t_end) cp.issue(kh, vh, t + 1, a.Lk, kn, vn);
     const int kind = wave_active ? tile_kind(t * kBc, kBc, w_span, a.window, a.Lk) : 0;
     if (kind != 0)
-      bf16_tile<D>(ks_, vs_, kbase, vbase, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
+      bf16_tile<D>(ks_, vs_, ka, va, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
   };
   for (int t = t_begin; t < t_end; t += 2) {
     step(t, K0, V0, K1, V1);
