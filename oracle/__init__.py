@@ -11,6 +11,8 @@ from .attention import (  # noqa: F401
     decode_partials,
     effective_scale,
     kv_head_of,
+    max_logit,
+    max_logit_rows,
     naive_sink_row_sum_f32,
     query_position,
     rebase_sink_f32,

@@ -33,6 +33,11 @@ GPU sees, i.e. bf16 or fp32 values upcast):
   the sink exactly once as one more logit (FlashMLA patch stack page, section
   3 "exact small-split combine").
 
+* ``max_logit_rows`` / ``max_logit`` -- the largest pre-softmax logit
+  scale*<q_i,k_j> over the keys each row sees (sink excluded), per row and
+  per head (flash-attention contribution-radar profile, task card for issue
+  #2986).
+
 * ``naive_sink_row_sum_f32`` / ``rebase_sink_f32`` -- the two sink updates of
   the cf-1.com page (fix two), evaluated in float32 so that tests can show the
   old additive form overflowing and the rebased form staying finite.
@@ -161,6 +166,54 @@ def attention_fwd(q, k, v, sinks, window: int, scale: float, block: int = 256):
                 out[b, h, r0:r0 + len(rows)] = o
                 lse[b, h, r0:r0 + len(rows)] = l
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# maximum pre-softmax logit
+# ---------------------------------------------------------------------------
+
+def max_logit_rows(q, k, b: int, h: int, rows, window: int, scale: float):
+    """Largest pre-softmax logit of selected query rows of (b, h).
+
+    The logit is the score that enters the softmax, s_ij = scale * <q_i, k_j>,
+    taken over the keys row i sees (the same causal/window/GQA rules as the
+    forward); the sink is a learned logit, not an entry of Q K^T, and is not
+    included.  A row that sees no key gives -inf.  (flash-attention
+    contribution-radar profile, task card for issue #2986: expose the maximum
+    pre-softmax logit of the forward pass, i.e. max of Q K^T rather than the
+    log-sum-exp, with causal masking and GQA.)
+    """
+    Hq, Lq = q.shape[1], q.shape[2]
+    Hkv, Lk = k.shape[1], k.shape[2]
+    kvh = kv_head_of(h, Hq, Hkv)
+    sc = effective_scale(scale)
+    out = []
+    for i in rows:
+        lo, hi = visible_range(query_position(int(i), Lq, Lk), Lk, window)
+        if hi <= lo:
+            out.append(-np.inf)
+            continue
+        qi = np.asarray(q[b, h, int(i)], dtype=np.float64)
+        kk = np.asarray(k[b, kvh, lo:hi], dtype=np.float64)
+        out.append(float((sc * (kk @ qi)).max()))
+    return np.array(out, dtype=np.float64)
+
+
+def max_logit(q, k, window: int, scale: float):
+    """Per-row [B,Hq,Lq] and per-head [B,Hq] maxima of the pre-softmax logit.
+
+    The per-head value is the maximum over the head's rows (the shape the
+    issue #2986 task card proposes); -inf where nothing is visible.
+    """
+    B, Hq, Lq, _ = q.shape
+    if Hq % k.shape[1]:
+        raise ValueError("Hq must be a multiple of Hkv")
+    row = np.full((B, Hq, Lq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            row[b, h] = max_logit_rows(q, k, b, h, range(Lq), window, scale)
+    head = row.max(axis=2) if Lq else np.full((B, Hq), -np.inf)
+    return row, head
 
 
 # ---------------------------------------------------------------------------

@@ -174,3 +174,88 @@ def err_split_combine(Lks=(1, 2, 63, 64, 65, 127, 129, 700, 1025), windows=(0, 5
             o, l = oracle.combine(op, lp, nv, sinks)
             worst = max(worst, np.abs(o - ref_o).max(), np.abs(l - ref_l).max())
     return worst
+
+
+# --- maximum pre-softmax logit ------------------------------------------------
+
+def brute_max_logit(q, k, window, scale):
+    """Per-row max of scale*<q_i,k_j> over visible keys, by Python loops (-inf if none)."""
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    sc = float(np.float32(scale))
+    out = np.full((B, Hq, Lq), -math.inf)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Lq):
+                pos = Lk - Lq + i
+                for j in range(Lk):
+                    if j > pos or (window > 0 and pos - j >= window):
+                        continue
+                    s = sc * math.fsum(q[b, h, i, d] * k[b, h // G, j, d] for d in range(D))
+                    out[b, h, i] = max(out[b, h, i], s)
+    return out
+
+
+def err_max_logit_brute(seed=0, B=2, Hq=4, Hkv=2, Lq=6, Lk=9, D=3, window=3):
+    q, k = rand((B, Hq, Lq, D), seed), rand((B, Hkv, Lk, D), seed + 1)
+    row, head = oracle.max_logit(q, k, window, 0.7)
+    want = brute_max_logit(q, k, window, 0.7)
+    return max(np.abs(row - want).max(), np.abs(head - want.max(axis=2)).max())
+
+
+def err_max_logit_ramp(Lq=37, Lk=50, window=7, scale=0.3, D=4):
+    """Keys along one direction u with k_j = (j + 1) u, queries q = u (resp. -u):
+    the row maximum is scale*(p + 1) at the last visible key p (resp.
+    -scale*(lo + 1) at the first visible key lo), exact in float64."""
+    u = np.zeros(D)
+    u[1] = 1.0
+    k = (np.arange(Lk, dtype=np.float64)[:, None] + 1.0) * u
+    k = k[None, None]
+    sc = float(np.float32(scale))
+    worst = 0.0
+    for sign in (1.0, -1.0):
+        q = np.broadcast_to(sign * u, (1, 1, Lq, D)).copy()
+        row, _ = oracle.max_logit(q, k, window, scale)
+        for i in range(Lq):
+            p = i + Lk - Lq
+            lo = max(0, p - window + 1) if window > 0 else 0
+            want = sc * (p + 1) if sign > 0 else -sc * (lo + 1)
+            worst = max(worst, abs(row[0, 0, i] - want))
+    return worst
+
+
+def err_max_logit_lse_bounds(seed=0, Hq=4, Hkv=2, Lq=40, Lk=60, D=8, window=9):
+    """Without a sink, max_j s_j <= LSE <= max_j s_j + ln(n) with n visible keys;
+    returns how far the oracle's maximum falls outside these bounds."""
+    q, k, v = rand((1, Hq, Lq, D), seed, 2.0), rand((1, Hkv, Lk, D), seed + 1), rand((1, Hkv, Lk, D), seed + 2)
+    row, _ = oracle.max_logit(q, k, window, 0.5)
+    _, lse = oracle.attention_fwd(q, k, v, None, window, 0.5)
+    n = np.array([visible_count(i, Lq, Lk, window) for i in range(Lq)], dtype=np.float64)
+    over = np.maximum(row - lse, 0.0)
+    under = np.maximum(lse - (row + np.log(n)), 0.0)
+    return max(over.max(), under.max())
+
+
+def err_max_logit_torch(seed=0, B=2, Hq=6, Hkv=3, Lq=50, Lk=70, D=16, window=13):
+    """torch: float64 matmul of repeated K heads, -inf where an index mask forbids, amax."""
+    q, k = rand((B, Hq, Lq, D), seed), rand((B, Hkv, Lk, D), seed + 1)
+    q_t = torch.from_numpy(q)
+    k_t = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1)
+    sc = float(np.float32(0.25))
+    s = sc * torch.matmul(q_t, k_t.transpose(-1, -2).contiguous())
+    pos = torch.arange(Lq).unsqueeze(1) + (Lk - Lq)
+    key = torch.arange(Lk).unsqueeze(0)
+    keep = key <= pos
+    if window > 0:
+        keep &= key > pos - window
+    want = s.masked_fill(~keep, -math.inf).amax(dim=-1).numpy()
+    row, head = oracle.max_logit(q, k, window, 0.25)
+    return max(np.abs(row - want).max(), np.abs(head - want.max(axis=2)).max())
+
+
+def err_max_logit_gqa(seed=0, Hq=8, Hkv=2, L=30, D=8, window=5):
+    q, k = rand((2, Hq, L, D), seed), rand((2, Hkv, L, D), seed + 1)
+    row, head = oracle.max_logit(q, k, window, 0.5)
+    row2, head2 = oracle.max_logit(q, np.repeat(k, Hq // Hkv, axis=1), window, 0.5)
+    return max(np.abs(row - row2).max(), np.abs(head - head2).max())

@@ -332,3 +332,60 @@ def test_pins_catch_split_mistakes(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(oa, "split_ranges", overlap)
         assert pins.err_split_combine(splits=(2, 7)) > 1e-6
+
+
+# --- maximum pre-softmax logit -------------------------------------------------
+
+@pytest.mark.parametrize("window", [0, 1, 3, 20])
+def test_max_logit_brute_force(window):
+    assert pins.err_max_logit_brute(window=window) < 1e-12
+    assert pins.err_max_logit_brute(window=window, Lq=4, Lk=9, Hq=3, Hkv=1) < 1e-12
+
+
+@pytest.mark.parametrize("window", [0, 1, 7, 100])
+def test_max_logit_ramp_closed_form(window):
+    assert pins.err_max_logit_ramp(window=window) < 1e-12
+
+
+def test_max_logit_within_lse_bounds():
+    assert pins.err_max_logit_lse_bounds() < 1e-12
+    assert pins.err_max_logit_lse_bounds(window=0, Lq=60, Lk=60) < 1e-12
+
+
+def test_max_logit_torch_masked_max():
+    assert pins.err_max_logit_torch() < 1e-12
+    assert pins.err_max_logit_torch(window=0) < 1e-12
+
+
+def test_max_logit_gqa_is_repeated_mha():
+    assert pins.err_max_logit_gqa() == 0.0
+
+
+def test_max_logit_ignores_sink_and_values():
+    q, k = pins.rand((1, 2, 5, 4), 1), pins.rand((1, 1, 5, 4), 2)
+    row, head = oracle.max_logit(q, k, 0, 0.5)
+    # row 0 sees only key 0; the last row sees every key
+    assert row[0, 0, 0] == pytest.approx(float(np.float32(0.5)) * float(q[0, 0, 0] @ k[0, 0, 0]), abs=1e-12)
+    assert head.shape == (1, 2) and np.all(head == row.max(axis=2))
+
+
+def _max_logit_caught(monkeypatch, name, fake):
+    with monkeypatch.context() as m:
+        m.setattr(oa, name, fake)
+        errs = [pins.err_max_logit_brute(window=3), pins.err_max_logit_ramp(window=7),
+                pins.err_max_logit_torch(), pins.err_max_logit_lse_bounds()]
+    return max(errs) > 1e-6
+
+
+def test_max_logit_pins_catch_index_mistakes(monkeypatch):
+    def one_more_key(p, Lk, window):
+        hi = min(p + 1, Lk)
+        lo = 0 if window <= 0 else max(0, p - window)
+        return lo, max(lo, hi)
+    assert _max_logit_caught(monkeypatch, "visible_range", one_more_key)
+    assert _max_logit_caught(monkeypatch, "query_position", lambda i, Lq, Lk: i)
+    assert _max_logit_caught(monkeypatch, "kv_head_of", lambda h, Hq, Hkv: h % Hkv)
+
+
+def test_max_logit_pins_catch_missing_scale(monkeypatch):
+    assert _max_logit_caught(monkeypatch, "effective_scale", lambda s: 1.0)
