@@ -195,6 +195,22 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
+    # attn_fwd_max_logit (per-row and per-head maxima) on the same prefill,
+    # timed like attn_fwd, to report what the extra outputs cost.
+    ml_row = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+    ml_head = torch.empty(lse.shape[:2], dtype=torch.float32, device=dev)
+    n_ml = max(10, args.steps // 5)
+    ml_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_ml)]
+    with torch.cuda.stream(stream):
+        for e0, e1 in ml_ev:
+            e0.record(stream)
+            A.attn_fwd_max_logit(q, k, v, s, out, lse, ml_row, ml_head, window=wp.window,
+                                 scale=wp.scale, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+    t_ml = np.array([e0.elapsed_time(e1) for e0, e1 in ml_ev[n_ml // 2:]]) * 1e-3
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -213,7 +229,7 @@ def main():
     tflops = flops / t_fwd.mean() / 1e12
     dbytes = decode_bytes(seqlens, wd.Hq, wd.Hkv, wd.D, wd.window)
     dec_gbps = dbytes / (t_dec.mean() + t_cmb.mean()) / 1e9
-    traffic = stored_traffic("fwd_bf16_kernel<128,false>:" + wp.name)
+    traffic = stored_traffic("fwd_bf16_kernel<128,false,false>:" + wp.name)
     dec_traffic = stored_traffic("decode_kernel<128>:" + wd.name)
     dec_only = dbytes / t_dec.mean() / 1e9
 
@@ -245,7 +261,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "fwd_bf16_kernel<128,false>",
+            "kernel": "fwd_bf16_kernel<128,false,false>",
             "ms_per_launch": round(t_fwd.mean() * 1e3, 4),
         },
         "decode": {
@@ -265,6 +281,12 @@ def main():
             "kernel": "decode_kernel<128>",
             "ms_per_launch": round(t_dec.mean() * 1e3, 4),
         },
+    }
+    res["max_logit"] = {
+        "entry": "attn_fwd_max_logit (row [B,Hq,Lq] and head [B,Hq] maxima)",
+        "ms_per_launch": round(t_ml.mean() * 1e3, 4),
+        "TFLOP/s": round(flops / t_ml.mean() / 1e12, 2),
+        "time_vs_attn_fwd": round(t_ml.mean() / t_fwd.mean(), 4),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wp, qh, kh, vh, sh)

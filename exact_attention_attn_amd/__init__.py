@@ -13,7 +13,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["attn_fwd", "attn_decode_splitkv", "attn_combine", "attn_strerror", "AttnError",
+__all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_combine", "attn_strerror", "AttnError",
            "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
 
 ATTN_BF16 = 0
@@ -31,6 +31,7 @@ _f = ctypes.c_float
 
 _SIGNATURES = {
     "attn_fwd": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp],
+    "attn_fwd_max_logit": [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp],
     "attn_decode_splitkv": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
     "attn_combine": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "attn_strerror": [_i],
@@ -133,6 +134,41 @@ def attn_fwd(q, k, v, sinks, out, lse=None, *, window: int = 0, scale: float | N
         _dev(out, "out"), _dev(lse, "lse", torch.float32), B, Hq, Hkv, Lq, Lk, D, int(window),
         float(scale), _dtype_code(q), _dtype_code(out), _stream(stream))
     _check("attn_fwd", rc)
+
+
+def attn_fwd_max_logit(q, k, v, sinks, out, lse=None, max_row=None, max_head=None, *,
+                       window: int = 0, scale: float | None = None, stream=None) -> None:
+    """attn_fwd plus the largest pre-softmax logit scale*<q,k> over the visible keys.
+
+    max_row [B,Hq,Lq] fp32 or None; max_head [B,Hq] fp32 or None (overwritten
+    with -inf on the stream, then raised atomically).  out and lse are those
+    of attn_fwd.
+    """
+    import torch
+
+    B, Hq, Lq, D = q.shape
+    _, Hkv, Lk, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/k/v/out")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if sinks is not None and tuple(sinks.shape) != (Hq,):
+        raise ValueError("sinks must be [Hq]")
+    if lse is not None and tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("lse must be [B,Hq,Lq]")
+    if max_row is not None and tuple(max_row.shape) != (B, Hq, Lq):
+        raise ValueError("max_row must be [B,Hq,Lq]")
+    if max_head is not None and tuple(max_head.shape) != (B, Hq):
+        raise ValueError("max_head must be [B,Hq]")
+    if scale is None:
+        scale = D ** -0.5
+    rc = load_library().attn_fwd_max_logit(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(sinks, "sinks", torch.float32),
+        _dev(out, "out"), _dev(lse, "lse", torch.float32),
+        _dev(max_row, "max_row", torch.float32), _dev(max_head, "max_head", torch.float32),
+        B, Hq, Hkv, Lq, Lk, D, int(window), float(scale), _dtype_code(q), _dtype_code(out),
+        _stream(stream))
+    _check("attn_fwd_max_logit", rc)
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_part, *,

@@ -61,9 +61,23 @@ int attn_fwd(const void* q, const void* k, const void* v, const float* sinks, vo
   if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
       (sinks && (reinterpret_cast<uintptr_t>(sinks) & 3u)))
     return ATTN_ERR_VALUE;
-  return from_hip(attn::launch_fwd(q, k, v, sinks, out, lse, B, Hq, Hkv, Lq, Lk, D, window, scale,
-                                   in_dtype == ATTN_F32, out_dtype == ATTN_F32,
+  return from_hip(attn::launch_fwd(q, k, v, sinks, out, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk,
+                                   D, window, scale, in_dtype == ATTN_F32, out_dtype == ATTN_F32,
                                    static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_max_logit(const void* q, const void* k, const void* v, const float* sinks, void* out,
+                       float* lse, float* max_logit_row, float* max_logit_head, int B, int Hq,
+                       int Hkv, int Lq, int Lk, int D, int window, float scale, int in_dtype,
+                       int out_dtype, void* stream) {
+  int rc = check_fwd(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, out_dtype);
+  if (rc != ATTN_OK) return rc;
+  for (const void* p : {(const void*)lse, (const void*)sinks, (const void*)max_logit_row,
+                        (const void*)max_logit_head})
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return ATTN_ERR_VALUE;
+  return from_hip(attn::launch_fwd(q, k, v, sinks, out, lse, max_logit_row, max_logit_head, B, Hq,
+                                   Hkv, Lq, Lk, D, window, scale, in_dtype == ATTN_F32,
+                                   out_dtype == ATTN_F32, static_cast<hipStream_t>(stream)));
 }
 
 int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,

@@ -50,18 +50,22 @@ __device__ __forceinline__ int tile_kind(int t0, int bc, RowSpan s, int window, 
 
 // Online-softmax state of the query column a lane owns.
 struct Row {
-  float m;  // reference max (log2 domain) of acc and l; -inf before any visible key
-  float l;  // partial sum of this lane half
+  float m;   // reference max (log2 domain) of acc and l; -inf before any visible key
+  float l;   // partial sum of this lane half
+  float mx;  // largest raw score <q, k> seen (kept only when the max logit is asked for)
 };
 
 // Update the running state with a tile of raw scores s (already masked to -inf),
 // turn s into probabilities in place and return the rescale factor for acc.
-template <int N>
+// With MAXL the exact running maximum of the raw scores is kept in row.mx
+// (row.m lags it by up to the rebase threshold).
+template <int N, bool MAXL>
 __device__ __forceinline__ float softmax_tile(float (&s)[N], Row& row, float c) {
   float mx = s[0];
 #pragma unroll
   for (int v = 1; v < N; ++v) mx = fmaxf(mx, s[v]);
   mx = pair_max(mx);
+  if (MAXL) row.mx = fmaxf(row.mx, mx);
   float m_new = fmaxf(row.m, mx * c);
   float alpha = 1.0f;
   bool need = m_new > row.m + kRebaseThreshold;  // false while m_new = -inf
@@ -125,10 +129,42 @@ struct FwdArgs {
   const float* sinks;
   void* out;
   float* lse;
+  float* max_row;   // [B,Hq,Lq] largest pre-softmax logit per row, or NULL
+  float* max_head;  // [B,Hq] largest per head (filled with -inf beforehand), or NULL
   int B, Hq, Hkv, Lq, Lk, window;
-  float c;  // scale * log2(e)
+  float c;      // scale * log2(e)
+  float scale;  // softmax scale (the logit is scale * <q, k>)
   int n_qtiles;
 };
+
+// Atomic maximum of a float held in global memory (no NaNs): a non-negative
+// float orders like its bits as a signed integer, a negative one inversely
+// to its bits as an unsigned integer, and -inf (the initial value) is below
+// every other value in both orders.
+__device__ __forceinline__ void atomic_max_f32(float* addr, float v) {
+  const int bits = __float_as_int(v);
+  if (bits >= 0)
+    atomicMax(reinterpret_cast<int*>(addr), bits);
+  else
+    atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+// Store the max pre-softmax logit of the wave's rows: per row (one lane per
+// row) and folded into the head's maximum (one atomic per wave).
+__device__ __forceinline__ void store_max_logit(const FwdArgs& a, const Row& row, int b, int h,
+                                                int my_row, bool valid, int half, int lane) {
+  const float ml = valid ? a.scale * row.mx : kNegInf;  // scale > 0
+  if (a.max_row && valid && half == 0) a.max_row[(size_t)(b * a.Hq + h) * a.Lq + my_row] = ml;
+  if (a.max_head) {
+    const float wm = wave_max(ml);
+    if (lane == 0 && wm != kNegInf) atomic_max_f32(a.max_head + b * a.Hq + h, wm);
+  }
+}
+
+__global__ void fill_kernel(float* p, int n, float value) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
 
 // Decode the work-group id into (b, h, q-tile); longest q-tiles first within
 // each (batch, KV head), and the G query heads of a KV head adjacent.
@@ -242,7 +278,7 @@ constexpr int kSgDsRead = 0x100;
 // O^T += V^T P^T.  Operand reads run ahead of the MFMAs that consume them
 // (the two S^T accumulators and the D/32 O^T accumulators are independent
 // chains, so consecutive MFMAs never wait on each other).
-template <int D>
+template <int D, bool MAXL>
 __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* vs_,
                                           const int (&ka)[D / 16], const int (&va)[2][D / 32],
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
@@ -308,7 +344,7 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
         s[kb * 16 + v] = (j - lo <= span) ? s[kb * 16 + v] : kNegInf;
       }
   }
-  float alpha = softmax_tile<32>(s, row, c);
+  float alpha = softmax_tile<32, MAXL>(s, row, c);
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] *= alpha;
@@ -376,7 +412,7 @@ __host__ __device__ __forceinline__ int bf_heads_per_group(int G) {
   return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool MAXL>
 __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using L = BfLayout<D>;
   using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
@@ -427,7 +463,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
-  Row row = {kNegInf, 0.0f};
+  Row row = {kNegInf, 0.0f, kNegInf};
   const int p = my_row + off_q;
   const int vis_hi = min(p, a.Lk - 1);
   const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
@@ -454,7 +490,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     if (t + 1 < t_end) cp.issue(kh, vh, t + 1, a.Lk, kn, vn);
     const int kind = wave_active ? tile_kind(t * kBc, kBc, w_span, a.window, a.Lk) : 0;
     if (kind != 0)
-      bf16_tile<D>(ks_, vs_, ka, va, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
+      bf16_tile<D, MAXL>(ks_, vs_, ka, va, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
   };
   for (int t = t_begin; t < t_end; t += 2) {
     step(t, K0, V0, K1, V1);
@@ -466,12 +502,13 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + h) * a.Lq + my_row) * D;
   float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + h) * a.Lq + my_row : nullptr;
   finalize_store<D / 32, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
+  if (MAXL) store_max_logit(a, row, wk.b, h, my_row, row_valid, half, lane);
 }
 
 // ------------------------------------------------------------------------
 // float32 inputs (v_mfma_f32_32x32x2_f32)
 // ------------------------------------------------------------------------
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool MAXL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   constexpr int BC = 32;
   constexpr int PITCH = D + 1;  // floats per LDS row (odd pitch spreads rows over banks)
@@ -512,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
-  Row row = {kNegInf, 0.0f};
+  Row row = {kNegInf, 0.0f, kNegInf};
   const int p = my_row + off_q;
   const int vis_hi = min(p, a.Lk - 1);
   const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
@@ -567,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
           s[v] = vis ? s[v] : kNegInf;
         }
       }
-      float alpha = softmax_tile<16>(s, row, a.c);
+      float alpha = softmax_tile<16, MAXL>(s, row, a.c);
       if (alpha != 1.0f) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] *= alpha;
@@ -587,6 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row) * D;
   float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + wk.h) * a.Lq + my_row : nullptr;
   finalize_store<NDB, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
+  if (MAXL) store_max_logit(a, row, wk.b, wk.h, my_row, row_valid, half, lane);
 }
 
 template <typename K>
@@ -596,32 +634,47 @@ hipError_t launch(K kernel, int threads, const FwdArgs& a, hipStream_t stream, i
   return hipGetLastError();
 }
 
+template <bool OUT, bool MAXL>
+hipError_t launch_typed(const FwdArgs& a, int D, bool in_f32, hipStream_t stream) {
+  if (!in_f32) {
+    const int HG = bf_heads_per_group(a.Hq / a.Hkv);
+    return D == 128 ? launch(fwd_bf16_kernel<128, OUT, MAXL>, kBfThreads, a, stream, HG)
+                    : launch(fwd_bf16_kernel<64, OUT, MAXL>, kBfThreads, a, stream, HG);
+  }
+  return D == 128 ? launch(fwd_f32_kernel<128, OUT, MAXL>, kThreads, a, stream, 1)
+                  : launch(fwd_f32_kernel<64, OUT, MAXL>, kThreads, a, stream, 1);
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* sinks, void* out,
-                      float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int D, int window,
-                      float scale, bool in_f32, bool out_f32, hipStream_t stream) {
+                      float* lse, float* max_row, float* max_head, int B, int Hq, int Hkv, int Lq,
+                      int Lk, int D, int window, float scale, bool in_f32, bool out_f32,
+                      hipStream_t stream) {
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.out = out; a.lse = lse;
+  a.max_row = max_row; a.max_head = max_head;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.window = window;
   a.c = scale * kLog2e;
+  a.scale = scale;
   if (!in_f32) {
-    const int HG = bf_heads_per_group(Hq / Hkv);
-    const int rows = kBfWaves / HG * kRowsPerWave;
+    const int rows = kBfWaves / bf_heads_per_group(Hq / Hkv) * kRowsPerWave;
     a.n_qtiles = (Lq + rows - 1) / rows;
-    const int t = kBfThreads;
-    if (D == 128) return out_f32 ? launch(fwd_bf16_kernel<128, true>, t, a, stream, HG)
-                                 : launch(fwd_bf16_kernel<128, false>, t, a, stream, HG);
-    return out_f32 ? launch(fwd_bf16_kernel<64, true>, t, a, stream, HG)
-                   : launch(fwd_bf16_kernel<64, false>, t, a, stream, HG);
+  } else {
+    a.n_qtiles = (Lq + kBr - 1) / kBr;
   }
-  a.n_qtiles = (Lq + kBr - 1) / kBr;
-  const int t = kThreads;
-  if (D == 128) return out_f32 ? launch(fwd_f32_kernel<128, true>, t, a, stream, 1)
-                               : launch(fwd_f32_kernel<128, false>, t, a, stream, 1);
-  return out_f32 ? launch(fwd_f32_kernel<64, true>, t, a, stream, 1)
-                 : launch(fwd_f32_kernel<64, false>, t, a, stream, 1);
+  const bool maxl = max_row || max_head;
+  if (max_head) {
+    const int n = B * Hq;
+    hipLaunchKernelGGL(fill_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, max_head, n,
+                       kNegInf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (out_f32) return maxl ? launch_typed<true, true>(a, D, in_f32, stream)
+                           : launch_typed<true, false>(a, D, in_f32, stream);
+  return maxl ? launch_typed<false, true>(a, D, in_f32, stream)
+              : launch_typed<false, false>(a, D, in_f32, stream);
 }
-
 
 }  // namespace attn

@@ -6,9 +6,13 @@
 
 namespace attn {
 
+// max_row / max_head (either may be NULL): largest pre-softmax logit per row
+// [B,Hq,Lq] and per head [B,Hq]; max_head is filled with -inf on the stream
+// first, then raised with atomics.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* sinks, void* out,
-                      float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int D, int window,
-                      float scale, bool in_f32, bool out_f32, hipStream_t stream);
+                      float* lse, float* max_row, float* max_head, int B, int Hq, int Hkv, int Lq,
+                      int Lk, int D, int window, float scale, bool in_f32, bool out_f32,
+                      hipStream_t stream);
 
 hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,

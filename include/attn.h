@@ -3,7 +3,9 @@
  *
  * Three calls form the path:
  *   attn_fwd             fused tiled attention forward (prefill): causal +
- *                        sliding window, GQA, learned per-head sink, LSE;
+ *                        sliding window, GQA, learned per-head sink, LSE
+ *                        (attn_fwd_max_logit: the same, plus the largest
+ *                        pre-softmax logit per row and per head);
  *   attn_decode_splitkv  split-KV decode: per-split partial outputs and LSEs;
  *   attn_combine         LSE-weighted merge of the valid splits, sink added once.
  *
@@ -70,6 +72,29 @@ enum {
 int attn_fwd(const void* q, const void* k, const void* v, const float* sinks, void* out,
              float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int D, int window, float scale,
              int in_dtype, int out_dtype, void* stream);
+
+/*
+ * attn_fwd_max_logit -- attn_fwd that also returns the largest pre-softmax
+ * logit (flash-attention contribution-radar profile, task card for issue
+ * #2986: expose the maximum pre-softmax logit of the forward pass, the max of
+ * the scores rather than their log-sum-exp, for training monitoring).
+ *
+ * The logit is the score that enters the softmax, scale * <q_i, k_j>, over
+ * the keys row i sees (same mask and GQA rules as attn_fwd); the sink is not
+ * a score and is excluded.  Every argument of attn_fwd keeps its meaning, and
+ * out/lse are bitwise those of attn_fwd.  Additionally:
+ * max_logit_row  [B, Hq, Lq] float32, or NULL: the row's maximum;
+ * max_logit_head [B, Hq]     float32, or NULL: the maximum over the head's
+ *                rows.  The call first overwrites it with -inf on the stream,
+ *                then raises it with atomic max operations (order-independent,
+ *                so the result is deterministic).
+ * Both NULL is allowed (then it is attn_fwd).  Extra pointers must be 4-byte
+ * aligned (ATTN_ERR_VALUE otherwise).
+ */
+int attn_fwd_max_logit(const void* q, const void* k, const void* v, const float* sinks, void* out,
+                       float* lse, float* max_logit_row, float* max_logit_head, int B, int Hq,
+                       int Hkv, int Lq, int Lk, int D, int window, float scale, int in_dtype,
+                       int out_dtype, void* stream);
 
 /*
  * attn_decode_splitkv -- one query per sequence over a KV cache, cut into splits.

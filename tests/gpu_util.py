@@ -57,6 +57,25 @@ def run_fwd(q, k, v, sinks, dtype, window, scale, out_f32=True, rows=None):
     return res
 
 
+def run_fwd_max_logit(q, k, v, sinks, dtype, window, scale, out_f32=True, want_row=True,
+                      want_head=True):
+    """Run attn_fwd_max_logit; return O, LSE, row maxima and head maxima (None if not asked)."""
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    sd = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
+    out = torch.empty(qd.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    mrow = torch.full(qd.shape[:3], float("nan"), device="cuda") if want_row else None
+    # stale contents must not leak: the call resets the head maxima itself
+    mhead = torch.full(qd.shape[:2], 1e30, device="cuda") if want_head else None
+    A.attn_fwd_max_logit(qd, kd, vd, sd, out, lse, mrow, mhead, window=window, scale=scale)
+    torch.cuda.synchronize()
+    res = (out.float().cpu().numpy(), lse.cpu().numpy(),
+           None if mrow is None else mrow.cpu().numpy(),
+           None if mhead is None else mhead.cpu().numpy())
+    del qd, kd, vd, out, lse, mrow, mhead
+    return res
+
+
 def compare(o, l, o_ref, l_ref, what: str, tol_max=TOL_MAX, tol_mean=TOL_MEAN, tol_lse=TOL_LSE,
             bf16_out=False):
     o = np.asarray(o, np.float64)

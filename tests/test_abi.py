@@ -32,8 +32,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_decode_splitkv", "attn_combine", "attn_strerror",
-                          "attn_version"}
+    assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_combine",
+                          "attn_strerror", "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.attn_version().decode().startswith("attn-mi355x")
@@ -64,6 +64,25 @@ def fwd(lib, **kw):
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
+
+
+def fwd_ml(lib, **kw):
+    a = dict(q=P, k=P, v=P, sinks=P, out=P, lse=P, mrow=P, mhead=P, B=1, Hq=8, Hkv=2, Lq=10,
+             Lk=10, D=128, window=0, scale=0.1, ind=0, outd=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_max_logit(a["q"], a["k"], a["v"], a["sinks"], a["out"], a["lse"],
+                                  a["mrow"], a["mhead"], a["B"], a["Hq"], a["Hkv"], a["Lq"],
+                                  a["Lk"], a["D"], a["window"], a["scale"], a["ind"], a["outd"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(Hq=7), 2), (dict(Lq=11), 2), (dict(D=96), 3),
+    (dict(scale=0.0), 4), (dict(q=P + 8), 4), (dict(lse=P + 2), 4), (dict(mrow=P + 2), 4),
+    (dict(mhead=P + 1), 4), (dict(sinks=P + 2), 4),
+])
+def test_fwd_max_logit_rejects(lib, kw, code):
+    assert fwd_ml(lib, **kw) == code
 
 
 def dec(lib, **kw):
