@@ -38,6 +38,11 @@ GPU sees, i.e. bf16 or fp32 values upcast):
   per head (flash-attention contribution-radar profile, task card for issue
   #2986).
 
+* ``plan_splits`` -- the number of splits per sequence chosen by a policy
+  (fixed count, fixed keys per split, or a workload-aware cost rule); the
+  FlashMLA patch stack page (section 1) gives the idea but no formula, so the
+  rule is the library's (include/attn.h) and only its arithmetic is checked.
+
 * ``naive_sink_row_sum_f32`` / ``rebase_sink_f32`` -- the two sink updates of
   the cf-1.com page (fix two), evaluated in float32 so that tests can show the
   old additive form overflowing and the rebased form staying finite.
@@ -248,6 +253,66 @@ def split_ranges(Lk: int, num_splits: int, window: int) -> list[tuple[int, int]]
         out.append((s0, min(s0 + chunk, Lk)))
         s0 += chunk
     return out
+
+
+# Split-count planning.  The FlashMLA patch stack page (section 1) describes a
+# workload-aware partition policy: gather the workload's shape, choose the
+# partition by policy (baseline / dynamic / fixed), reject what is illegal.
+# The pages give no formula; the rule below is this library's, stated in
+# include/attn.h, and restated here step by step.
+PLAN_COUNT, PLAN_KEYS, PLAN_AUTO = "count", "keys", "auto"
+PLAN_CHUNKS = (256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
+PLAN_ITEM_COST = 96  # per-item overhead of the decode, in key rows
+
+
+def visible_keys(seqlen: int, Lk_max: int, window: int) -> int:
+    """Keys the decode query of a sequence sees after clamping Lk to [0, Lk_max]."""
+    Lk = min(max(int(seqlen), 0), Lk_max)
+    lo = max(0, Lk - window) if window > 0 else 0
+    return Lk - lo
+
+
+def plan_splits(seqlens, Hq: int, Hkv: int, Lk_max: int, window: int, max_splits: int,
+                policy: str, param: int, slots: int) -> list[int]:
+    """num_splits per sequence under a policy.
+
+    count: every sequence gets param splits; keys: ceil(n/param) splits for n
+    visible keys; auto: the chunk target c from PLAN_CHUNKS that minimises
+        min(per * Z, ceil(T / S) + Z) + PLAN_ITEM_COST * per,
+    per = ceil(I / S), where for target c every sequence takes ceil(n/c)
+    splits, I counts the decode's work items (valid splits x KV heads x
+    query-column groups of 32), Z is the largest split in keys, T the visible
+    key rows times KV heads and groups, and S the number of work-groups the
+    decode runs (slots).  The first such c wins.  Splits are clamped to
+    [1, max_splits] in every policy.
+    """
+    ns_of = lambda n, c: min(max(-(-n // c), 1), max_splits)
+    ns_clamp = lambda x: min(max(int(x), 1), max_splits)
+    lens = [visible_keys(x, Lk_max, window) for x in seqlens]
+    if policy == PLAN_COUNT:
+        return [ns_clamp(param) for _ in lens]
+    if policy == PLAN_KEYS:
+        return [ns_of(n, int(param)) for n in lens]
+    if policy != PLAN_AUTO:
+        raise ValueError(policy)
+    G = Hq // Hkv
+    hq = Hkv * (-(-G // 32))
+    T = hq * sum(lens)
+    best = None
+    for c in PLAN_CHUNKS:
+        items, z = 0, 0
+        for n in lens:
+            if n == 0:
+                continue
+            parts = split_ranges(n, ns_of(n, c), 0)
+            items += len(parts)
+            z = max(z, max(e - a for a, e in parts))
+        items *= hq
+        per = -(-items // slots)
+        cost = min(per * z, -(-T // slots) + z) + PLAN_ITEM_COST * per
+        if best is None or cost < best[0]:
+            best = (cost, c)
+    return [ns_of(n, best[1]) for n in lens]
 
 
 def decode_partials(q, k_cache, v_cache, seqlens, num_splits, window: int, scale: float,

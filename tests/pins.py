@@ -259,3 +259,64 @@ def err_max_logit_gqa(seed=0, Hq=8, Hkv=2, L=30, D=8, window=5):
     row, head = oracle.max_logit(q, k, window, 0.5)
     row2, head2 = oracle.max_logit(q, np.repeat(k, Hq // Hkv, axis=1), window, 0.5)
     return max(np.abs(row - row2).max(), np.abs(head - head2).max())
+
+
+# --- split-count planning -------------------------------------------------------
+
+# The planning rule as include/attn.h states it, retyped here on purpose so
+# that a changed constant in the oracle shows up.
+RULE_CHUNKS = (256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
+RULE_ITEM_COST = 96
+
+
+def brute_plan_auto(seqlens, Hq, Hkv, Lk_max, window, max_splits, slots):
+    """The auto policy by walking every split of every sequence key by key."""
+    G = Hq // Hkv
+    hq = Hkv * ((G + 31) // 32)
+    lens = []
+    for x in seqlens:
+        Lk = min(max(int(x), 0), Lk_max)
+        lo = max(0, Lk - window) if window > 0 else 0
+        lens.append(Lk - lo)
+    total = hq * sum(lens)
+    best_cost, best_c = None, None
+    for c in RULE_CHUNKS:
+        items, zmax = 0, 0
+        for n in lens:
+            if n == 0:
+                continue
+            ns = min(max(math.ceil(n / c), 1), max_splits)
+            chunk = math.ceil(math.ceil(n / ns) / 64) * 64
+            start = 0
+            while start < n:                      # one split per step
+                size = min(chunk, n - start)
+                items += 1
+                zmax = max(zmax, size)
+                start += chunk
+        items *= hq
+        per = math.ceil(items / slots)
+        cost = min(per * zmax, math.ceil(total / slots) + zmax) + RULE_ITEM_COST * per
+        if best_cost is None or cost < best_cost:
+            best_cost, best_c = cost, c
+    return [min(max(math.ceil(n / best_c), 1), max_splits) for n in lens]
+
+
+def err_plan(seed=0, B=40, Lk_max=5000, window=0, Hq=64, Hkv=8, max_splits=64, slots=512):
+    """Number of sequences whose planned split count differs from the
+    closed forms (count, keys) and the brute-force auto rule."""
+    rng = np.random.default_rng(seed)
+    seqlens = list(rng.integers(-5, Lk_max + 300, B))
+    bad = 0
+    for p in (1, 7, 64, 100):
+        got = oracle.plan_splits(seqlens, Hq, Hkv, Lk_max, window, max_splits, "count", p, slots)
+        bad += sum(g != min(max(p, 1), max_splits) for g in got)
+    for p in (64, 100, 1024):
+        got = oracle.plan_splits(seqlens, Hq, Hkv, Lk_max, window, max_splits, "keys", p, slots)
+        for g, x in zip(got, seqlens):
+            Lk = min(max(int(x), 0), Lk_max)
+            n = Lk - (max(0, Lk - window) if window > 0 else 0)
+            bad += g != min(max(math.ceil(n / p), 1), max_splits)
+    got = oracle.plan_splits(seqlens, Hq, Hkv, Lk_max, window, max_splits, "auto", 0, slots)
+    want = brute_plan_auto(seqlens, Hq, Hkv, Lk_max, window, max_splits, slots)
+    bad += sum(g != w for g, w in zip(got, want))
+    return bad

@@ -389,3 +389,36 @@ def test_max_logit_pins_catch_index_mistakes(monkeypatch):
 
 def test_max_logit_pins_catch_missing_scale(monkeypatch):
     assert _max_logit_caught(monkeypatch, "effective_scale", lambda s: 1.0)
+
+
+# --- split-count planning --------------------------------------------------------
+
+@pytest.mark.parametrize("seed,B,Lk_max,window,Hq,Hkv,max_splits,slots", [
+    (0, 40, 5000, 0, 64, 8, 64, 512), (1, 64, 32768, 0, 64, 8, 64, 512),
+    (2, 3, 32768, 513, 64, 8, 64, 512), (3, 256, 2048, 0, 64, 8, 64, 512),
+    (4, 16, 32768, 0, 64, 64, 64, 512), (5, 9, 100000, 0, 8, 1, 17, 77),
+    (6, 1, 131072, 0, 64, 8, 64, 512), (7, 33, 9000, 1000, 40, 1, 64, 256),
+])
+def test_plan_matches_rule(seed, B, Lk_max, window, Hq, Hkv, max_splits, slots):
+    assert pins.err_plan(seed, B, Lk_max, window, Hq, Hkv, max_splits, slots) == 0
+
+
+def test_plan_properties():
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        sl = list(rng.integers(0, 40000, int(rng.integers(1, 80))))
+        ns = oracle.plan_splits(sl, 64, 8, 32768, 0, 64, "auto", 0, 512)
+        assert all(1 <= x <= 64 for x in ns)
+        # uniform lengths -> one chunk target for all: equal split counts
+    assert len(set(oracle.plan_splits([20000] * 10, 64, 8, 32768, 0, 64, "auto", 0, 512))) == 1
+    # empty sequences still get one (empty) split
+    assert oracle.plan_splits([0, -3], 64, 8, 100, 0, 64, "auto", 0, 512) == [1, 1]
+
+
+def test_plan_pins_catch_changed_rule(monkeypatch):
+    with monkeypatch.context() as m:
+        m.setattr(oa, "PLAN_ITEM_COST", 0)
+        assert pins.err_plan(1, 64, 32768) > 0
+    with monkeypatch.context() as m:
+        m.setattr(oa, "PLAN_CHUNKS", (512, 1024, 2048))
+        assert pins.err_plan(1, 64, 32768) > 0
