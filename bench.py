@@ -82,6 +82,70 @@ def decode_bytes(seqlens, Hq, Hkv, D, window) -> int:
     return kv + B * Hq * D * 2 + B * Hq * D * 2 + B * Hq * 4 + Hq * 4
 
 
+def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd,
+                           seqlens, reps=20):
+    """GB/s of decode + combine under several split-count policies.
+
+    Rows: the decode workload of the step, and two synthetic mixes drawn on
+    the device (4 sequences of 32768 keys; 256 sequences of 128..2048 keys).
+    'auto' times attn_decode_plan + decode + combine; fixed rules time
+    decode + combine with counts planned beforehand.
+    """
+    def timed(q_, k_, v_, sl_, Lk_max, policy, param, nbytes):
+        B, Hq = q_.shape[0], q_.shape[1]
+        ns = torch.empty(B, dtype=torch.int32, device=dev)
+        plan = lambda: A.attn_decode_plan(sl_, ns, Hq=Hq, Hkv=k_.shape[1], Lk_max=Lk_max,
+                                          policy=policy, param=param, stream=stream)
+        if B == op.shape[0]:
+            o_, l_, out_, lse_ = op, lp, dout, dlse
+        else:
+            o_ = torch.empty((B,) + tuple(op.shape[1:]), dtype=op.dtype, device=dev)
+            l_ = torch.empty((B,) + tuple(lp.shape[1:]), dtype=lp.dtype, device=dev)
+            out_ = torch.empty((B,) + tuple(dout.shape[1:]), dtype=dout.dtype, device=dev)
+            lse_ = torch.empty((B,) + tuple(dlse.shape[1:]), dtype=dlse.dtype, device=dev)
+
+        def once():
+            if policy == "auto":
+                plan()
+            A.attn_decode_splitkv(q_, k_, v_, sl_, ns, o_, l_, window=0, scale=wd.scale,
+                                  stream=stream)
+            A.attn_combine(o_, l_, sl_, ns, ds, out_, lse_, Lk_max=Lk_max, window=0,
+                           stream=stream)
+        with torch.cuda.stream(stream):
+            plan()
+            for _ in range(5):
+                once()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                once()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return {"policy": f"{policy}({param})" if policy != "auto" else "auto",
+                "us": round(ms * 1e3, 1), "GB/s": round(nbytes / ms / 1e6, 1),
+                "total_splits": int(ns.sum().item())}
+
+    rows = []
+    Hq, Hkv, D = wd.Hq, wd.Hkv, wd.D
+    mixes = [("splitkv_decode", qd, kd, vd, sl, wd.Lk_max, np.asarray(seqlens))]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    for name, lens, Lk_max in (("B4 Lk32768", np.full(4, 32768), 32768),
+                               ("B256 Lk128-2048", np.random.default_rng(7).integers(128, 2049, 256), 2048)):
+        B = len(lens)
+        q_ = torch.randn(B, Hq, 1, D, device=dev, generator=g).to(torch.bfloat16)
+        k_ = torch.randn(B, Hkv, Lk_max, D, device=dev, generator=g).to(torch.bfloat16)
+        v_ = torch.randn(B, Hkv, Lk_max, D, device=dev, generator=g).to(torch.bfloat16)
+        mixes.append((name, q_, k_, v_, torch.from_numpy(lens.astype(np.int32)).to(dev), Lk_max, lens))
+    for name, q_, k_, v_, sl_, Lk_max, lens in mixes:
+        nbytes = decode_bytes(lens, Hq, Hkv, D, 0)
+        res = [timed(q_, k_, v_, sl_, Lk_max, pol, par, nbytes)
+               for pol, par in (("auto", 0), ("keys", 1024), ("keys", 512), ("count", 1))]
+        rows.append({"workload": name, "results": res})
+    return rows
+
+
 def cpu_baseline(w, q, k, v, sinks, budget_s=20.0):
     """Time the float64 oracle on whole heads of the prefill until ~budget_s of work."""
     import oracle
@@ -195,6 +259,12 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
+    # Split-count policies (attn_decode_plan): decode + combine GB/s with the
+    # workload-aware plan (the plan kernel inside the timed span) against
+    # fixed rules, on the decode workload above and two more batch/length mixes.
+    split_policy = measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp,
+                                          dout, dlse, wd, seqlens)
+
     # attn_fwd_max_logit (per-row and per-head maxima) on the same prefill,
     # timed like attn_fwd, to report what the extra outputs cost.
     ml_row = torch.empty(lse.shape, dtype=torch.float32, device=dev)
@@ -282,6 +352,7 @@ def main():
             "ms_per_launch": round(t_dec.mean() * 1e3, 4),
         },
     }
+    res["split_policy"] = split_policy
     res["max_logit"] = {
         "entry": "attn_fwd_max_logit (row [B,Hq,Lq] and head [B,Hq] maxima)",
         "ms_per_launch": round(t_ml.mean() * 1e3, 4),

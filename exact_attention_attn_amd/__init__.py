@@ -13,12 +13,13 @@ import ctypes
 import os
 import threading
 
-__all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_combine", "attn_strerror", "AttnError",
+__all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_decode_plan", "attn_combine", "attn_strerror", "AttnError",
            "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
 
 ATTN_BF16 = 0
 ATTN_F32 = 1
 MAX_SPLITS = 64
+SPLITS_POLICIES = {"auto": 0, "keys": 1, "count": 2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libattn_mi355x.so"
@@ -34,6 +35,7 @@ _SIGNATURES = {
     "attn_fwd_max_logit": [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp],
     "attn_decode_splitkv": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
     "attn_combine": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "attn_decode_plan": [_vp, _vp] + [_i] * 8 + [_vp],
     "attn_strerror": [_i],
     "attn_version": [],
 }
@@ -198,6 +200,29 @@ def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_
         B, Hq, Hkv, Lk_max, D, max_splits, int(window), float(scale), _dtype_code(q),
         _stream(stream))
     _check("attn_decode_splitkv", rc)
+
+
+def attn_decode_plan(seqlens_k, num_splits, *, Hq: int, Hkv: int, Lk_max: int,
+                     max_splits: int = MAX_SPLITS, window: int = 0, policy: str = "auto",
+                     param: int = 0, stream=None) -> None:
+    """Write num_splits [B] int32 for attn_decode_splitkv on the device.
+
+    policy "count" (param splits each), "keys" (ceil(n/param) splits for n
+    visible keys) or "auto" (workload-aware rule; param = work-group count of
+    the decode, 0 for the library's own), as include/attn.h states.
+    """
+    import torch
+
+    B = seqlens_k.shape[0]
+    if tuple(num_splits.shape) != (B,):
+        raise ValueError("num_splits must be [B]")
+    if policy not in SPLITS_POLICIES:
+        raise ValueError(f"policy must be one of {sorted(SPLITS_POLICIES)}")
+    rc = load_library().attn_decode_plan(
+        _dev(seqlens_k, "seqlens_k", torch.int32), _dev(num_splits, "num_splits", torch.int32),
+        B, int(Hq), int(Hkv), int(Lk_max), int(max_splits), int(window), SPLITS_POLICIES[policy],
+        int(param), _stream(stream))
+    _check("attn_decode_plan", rc)
 
 
 def attn_combine(o_part, lse_part, seqlens_k, num_splits, sinks, out, lse=None, *, Lk_max: int,

@@ -101,6 +101,21 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                                       static_cast<hipStream_t>(stream)));
 }
 
+int attn_decode_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int Hq, int Hkv,
+                     int Lk_max, int max_splits, int window, int policy, int param, void* stream) {
+  if (!seqlens_k || !num_splits) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lk_max < 1) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || max_splits < 1 || max_splits > ATTN_MAX_SPLITS || B > 65535 || Hq > 65535)
+    return ATTN_ERR_SHAPE;
+  if (policy != ATTN_SPLITS_AUTO && policy != ATTN_SPLITS_KEYS && policy != ATTN_SPLITS_COUNT)
+    return ATTN_ERR_UNSUPPORTED;
+  if (policy == ATTN_SPLITS_AUTO ? param < 0 : param < 1) return ATTN_ERR_VALUE;
+  if ((reinterpret_cast<uintptr_t>(seqlens_k) & 3u) || (reinterpret_cast<uintptr_t>(num_splits) & 3u))
+    return ATTN_ERR_VALUE;
+  return from_hip(attn::launch_plan(seqlens_k, num_splits, B, Hq, Hkv, Lk_max, max_splits, window,
+                                    policy, param, static_cast<hipStream_t>(stream)));
+}
+
 int attn_combine(const float* o_part, const float* lse_part, const int32_t* seqlens_k,
                  const int32_t* num_splits, const float* sinks, void* out, float* lse, int B,
                  int Hq, int D, int Lk_max, int max_splits, int window, int out_dtype,
@@ -124,8 +139,8 @@ const char* attn_strerror(int code) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "null pointer argument";
     case ATTN_ERR_SHAPE: return "invalid shape (sizes, head ratio, Lq > Lk or max_splits)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim or dtype";
-    case ATTN_ERR_VALUE: return "invalid value (scale or pointer alignment)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, dtype or policy";
+    case ATTN_ERR_VALUE: return "invalid value (scale, policy parameter or pointer alignment)";
     case ATTN_ERR_HIP: return "HIP launch failed";
     default: return "unknown error code";
   }

@@ -15,6 +15,7 @@
 // split s; only the n_valid splits that exist are loaded (FlashMLA patch
 // stack page, section 3: no masked work for splits that do not exist, real
 // splits accumulated in their order).  The sink joins as one more logit.
+#include "attn.h"
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -402,6 +403,99 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombArgs a) {
   if (a.lse && lane == 0) a.lse[bh] = lse_out;
 }
 
+// ---------------------------------------------------------------------------
+// Split-count planning (attn_decode_plan).  One work-group; for the auto
+// policy every thread accumulates, over its sequences, the item count and the
+// largest split of each candidate chunk target, then thread 0 picks the
+// target of least estimated cost (rule stated in include/attn.h).
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 256;
+constexpr int kPlanCands = 11;
+__constant__ int kPlanChunks[kPlanCands] = {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192};
+constexpr long long kPlanItemCost = 96;  // per-item overhead, in key rows
+
+struct PlanArgs {
+  const int32_t* seqlens;
+  int32_t* nsplits;
+  int B, Lk_max, max_splits, window, policy, param, slots, hq;
+};
+
+__device__ __forceinline__ int visible_n(int seqlen, int Lk_max, int window) {
+  const int Lk = min(max(seqlen, 0), Lk_max);
+  return Lk - (window > 0 ? max(0, Lk - window) : 0);
+}
+__device__ __forceinline__ int splits_for(int n, int target, int max_splits) {
+  return min(max((n + target - 1) / target, 1), max_splits);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ long long s_items[kPlanCands][kPlanThreads / 64];
+  __shared__ int s_z[kPlanCands][kPlanThreads / 64];
+  __shared__ long long s_T[kPlanThreads / 64];
+  __shared__ int s_target;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.policy == ATTN_SPLITS_AUTO) {
+    long long items[kPlanCands];
+    int z[kPlanCands];
+#pragma unroll
+    for (int i = 0; i < kPlanCands; ++i) { items[i] = 0; z[i] = 0; }
+    long long T = 0;
+    for (int b = tid; b < a.B; b += kPlanThreads) {
+      const int n = visible_n(a.seqlens[b], a.Lk_max, a.window);
+      T += n;
+      if (n == 0) continue;
+#pragma unroll
+      for (int i = 0; i < kPlanCands; ++i) {
+        const int ns = splits_for(n, kPlanChunks[i], a.max_splits);
+        const int chunk = ((n + ns - 1) / ns + 63) / 64 * 64;
+        items[i] += (n + chunk - 1) / chunk;
+        z[i] = max(z[i], min(chunk, n));
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      T += __shfl_xor(T, o);
+#pragma unroll
+      for (int i = 0; i < kPlanCands; ++i) {
+        items[i] += __shfl_xor(items[i], o);
+        z[i] = max(z[i], __shfl_xor(z[i], o));
+      }
+    }
+    if (lane == 0) {
+      s_T[wave] = T;
+#pragma unroll
+      for (int i = 0; i < kPlanCands; ++i) { s_items[i][wave] = items[i]; s_z[i][wave] = z[i]; }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      long long tot = 0;
+      for (int w = 0; w < kPlanThreads / 64; ++w) tot += s_T[w];
+      tot *= a.hq;
+      const long long S = a.slots;
+      long long best = -1;
+      int target = kPlanChunks[0];
+      for (int i = 0; i < kPlanCands; ++i) {
+        long long it = 0;
+        int zz = 0;
+        for (int w = 0; w < kPlanThreads / 64; ++w) { it += s_items[i][w]; zz = max(zz, s_z[i][w]); }
+        it *= a.hq;
+        const long long per = (it + S - 1) / S;
+        const long long cost = min(per * zz, (tot + S - 1) / S + zz) + kPlanItemCost * per;
+        if (best < 0 || cost < best) { best = cost; target = kPlanChunks[i]; }
+      }
+      s_target = target;
+    }
+    __syncthreads();
+  }
+  const int target = a.policy == ATTN_SPLITS_AUTO ? s_target : a.param;
+  for (int b = tid; b < a.B; b += kPlanThreads) {
+    const int ns = a.policy == ATTN_SPLITS_COUNT
+                       ? min(max(a.param, 1), a.max_splits)
+                       : splits_for(visible_n(a.seqlens[b], a.Lk_max, a.window), target, a.max_splits);
+    a.nsplits[b] = ns;
+  }
+}
+
 }  // namespace
 
 // Compute units of the current device, read once per device.
@@ -436,6 +530,21 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
     hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int Hq, int Hkv,
+                       int Lk_max, int max_splits, int window, int policy, int param,
+                       hipStream_t stream) {
+  PlanArgs a;
+  a.seqlens = seqlens_k; a.nsplits = num_splits;
+  a.B = B; a.Lk_max = Lk_max; a.max_splits = max_splits; a.window = window;
+  a.policy = policy; a.param = param;
+  // the decode's own grid: launch_decode runs 2 work-groups per compute unit
+  a.slots = (policy == ATTN_SPLITS_AUTO && param > 0) ? param : 2 * cu_count();
+  const int G = Hq / Hkv;
+  a.hq = Hkv * ((G + 31) / 32);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,11 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
                          float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
                          int max_splits, int window, float scale, hipStream_t stream);
 
+// num_splits[b] from seqlens_k by policy (ATTN_SPLITS_*); one work-group.
+hipError_t launch_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int Hq, int Hkv,
+                       int Lk_max, int max_splits, int window, int policy, int param,
+                       hipStream_t stream);
+
 hipError_t launch_combine(const float* o_part, const float* lse_part, const int32_t* seqlens_k,
                           const int32_t* num_splits, const float* sinks, void* out, float* lse,
                           int B, int Hq, int D, int Lk_max, int max_splits, int window,

@@ -6,7 +6,8 @@
  *                        sliding window, GQA, learned per-head sink, LSE
  *                        (attn_fwd_max_logit: the same, plus the largest
  *                        pre-softmax logit per row and per head);
- *   attn_decode_splitkv  split-KV decode: per-split partial outputs and LSEs;
+ *   attn_decode_splitkv  split-KV decode: per-split partial outputs and LSEs
+ *                        (attn_decode_plan: split counts chosen on the device);
  *   attn_combine         LSE-weighted merge of the valid splits, sink added once.
  *
  * Conventions shared by every call
@@ -57,6 +58,9 @@ enum {
 
 #define ATTN_SPLIT_ALIGN 64  /* split boundaries: multiples of 64 keys from the window start */
 #define ATTN_MAX_SPLITS 64
+
+/* Split-count policies of attn_decode_plan. */
+enum { ATTN_SPLITS_AUTO = 0, ATTN_SPLITS_KEYS = 1, ATTN_SPLITS_COUNT = 2 };
 
 /*
  * attn_fwd -- O = softmax(scale * Q K^T + mask, sink) V, and LSE.
@@ -122,6 +126,38 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
                         float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
                         int max_splits, int window, float scale, int in_dtype, void* stream);
+
+/*
+ * attn_decode_plan -- choose num_splits[b] for attn_decode_splitkv on the
+ * device, from seqlens_k and the shape, with no host synchronisation.
+ *
+ * Workload-aware partitioning (FlashMLA patch stack page, section 1: gather
+ * the workload's shape, pick the partition by policy -- baseline, dynamic or
+ * fixed -- and refuse what is illegal); the pages give no formula, the rules
+ * below are this library's.  n_b is the number of keys sequence b's query
+ * sees (Lk clamped to [0, Lk_max], window applied), and every result is
+ * clamped to [1, max_splits]:
+ *   ATTN_SPLITS_COUNT  num_splits[b] = param                      (param >= 1)
+ *   ATTN_SPLITS_KEYS   num_splits[b] = ceil(n_b / param)          (param >= 1)
+ *   ATTN_SPLITS_AUTO   num_splits[b] = ceil(n_b / c) for the chunk target c in
+ *                      {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096,
+ *                      6144, 8192} that minimises
+ *                        min(per * Z, ceil(T / S) + Z) + 96 * per,
+ *                      per = ceil(I / S), with, for target c: I the decode's
+ *                      work items (valid splits x Hkv x ceil((Hq/Hkv)/32)),
+ *                      Z the largest split in keys, T = sum_b n_b x Hkv x
+ *                      ceil((Hq/Hkv)/32) and S the decode's work-groups
+ *                      (param, or 2 x compute units when param = 0).  The
+ *                      first (smallest) such c wins.  The estimate is the
+ *                      keys of the most loaded work-group plus a per-item
+ *                      overhead of 96 key rows, both measured on MI355X.
+ * seqlens_k [B] int32 (device); num_splits [B] int32 (device, written).
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (sizes as in attn_decode_splitkv),
+ * ATTN_ERR_UNSUPPORTED (unknown policy), ATTN_ERR_VALUE (param < 1 for
+ * COUNT/KEYS, param < 0 for AUTO, misaligned pointer).
+ */
+int attn_decode_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int Hq, int Hkv,
+                     int Lk_max, int max_splits, int window, int policy, int param, void* stream);
 
 /*
  * attn_combine -- merge the valid split partials of each (b, h), sink once.

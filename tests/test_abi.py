@@ -32,8 +32,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_combine",
-                          "attn_strerror", "attn_version"}
+    assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_decode_plan",
+                          "attn_combine", "attn_strerror", "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.attn_version().decode().startswith("attn-mi355x")
@@ -134,3 +134,20 @@ def test_binding_rejects_host_tensors():
     k = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         A.attn_fwd(q, k, k, None, q.clone())
+
+
+def plan(lib, **kw):
+    a = dict(sl=P, ns=P, B=4, Hq=8, Hkv=2, Lk=100, ms=64, window=0, policy=0, param=0, stream=None)
+    a.update(kw)
+    return lib.attn_decode_plan(a["sl"], a["ns"], a["B"], a["Hq"], a["Hkv"], a["Lk"], a["ms"],
+                                a["window"], a["policy"], a["param"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sl=None), 1), (dict(ns=None), 1), (dict(B=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(ms=0), 2),
+    (dict(ms=65), 2), (dict(Lk=0), 2), (dict(B=70000), 2), (dict(policy=3), 3), (dict(policy=-1), 3),
+    (dict(policy=0, param=-1), 4), (dict(policy=1, param=0), 4), (dict(policy=2, param=0), 4),
+    (dict(sl=P + 2), 4), (dict(ns=P + 1), 4),
+])
+def test_plan_rejects(lib, kw, code):
+    assert plan(lib, **kw) == code
