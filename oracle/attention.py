@@ -38,6 +38,11 @@ GPU sees, i.e. bf16 or fp32 values upcast):
   per head (flash-attention contribution-radar profile, task card for issue
   #2986).
 
+* ``gather_paged`` / ``decode_paged`` / ``attention_fwd_varlen`` -- the
+  serving layouts: a KV cache held in pages named by a block table, and a
+  packed batch of sequences of different lengths delimited by cu_seqlens
+  (flash-attention profile: paged KV and varlen among its capabilities).
+
 * ``plan_splits`` -- the number of splits per sequence chosen by a policy
   (fixed count, fixed keys per split, or a workload-aware cost rule); the
   FlashMLA patch stack page (section 1) gives the idea but no formula, so the
@@ -392,6 +397,70 @@ def decode(q, k_cache, v_cache, seqlens, sinks, window: int, scale: float):
             o, l = attention_rows(q[b:b + 1], kk, vv, sinks, 0, h, [0], window, scale)
             out[b, h] = o[0]
             lse[b, h] = l[0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# paged KV caches and variable-length batches (the serving layouts: the
+# flash-attention profile lists paged KV -- block_table -- for decode and
+# varlen batches described by cu_seqlens among its capabilities and call flow)
+# ---------------------------------------------------------------------------
+
+def page_slot(j: int, page_size: int) -> tuple[int, int]:
+    """(block-table slot, row within the page) that holds key j."""
+    return j // page_size, j % page_size
+
+
+def gather_paged(pages, block_table, seqlens, page_size: int, Lk_max: int):
+    """Dense cache [B,Hkv,Lk_max,D] of a paged one.
+
+    pages [num_pages,Hkv,page_size,D]; block_table [B,max_pages] ints; key j
+    of sequence b is row j % page_size of page block_table[b, j // page_size].
+    Rows at or past seqlens[b] (clamped to [0, Lk_max]) stay NaN: no
+    computation may read them.
+    """
+    pages = np.asarray(pages, dtype=np.float64)
+    B = len(seqlens)
+    _, Hkv, _, D = pages.shape
+    dense = np.full((B, Hkv, Lk_max, D), np.nan)
+    for b in range(B):
+        Lk = min(max(int(seqlens[b]), 0), Lk_max)
+        for j in range(Lk):
+            slot, row = page_slot(j, page_size)
+            dense[b, :, j] = pages[int(block_table[b][slot]), :, row]
+    return dense
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, sinks, window: int, scale: float,
+                 page_size: int, Lk_max: int):
+    """Unsplit decode over a paged cache: the decode of the gathered cache."""
+    kc = gather_paged(k_pages, block_table, seqlens, page_size, Lk_max)
+    vc = gather_paged(v_pages, block_table, seqlens, page_size, Lk_max)
+    sl = [min(max(int(x), 0), Lk_max) for x in seqlens]
+    return decode(q, kc, vc, sl, sinks, window, scale)
+
+
+def attention_fwd_varlen(q, k, v, cu_q, cu_k, sinks, window: int, scale: float):
+    """Attention over a packed batch of sequences of different lengths.
+
+    q [Hq,total_q,D], k/v [Hkv,total_k,D]; sequence b owns query rows
+    cu_q[b]..cu_q[b+1] and keys cu_k[b]..cu_k[b+1].  Within a sequence the
+    rules of ``attention_fwd`` hold (its queries are its last Lq_b positions;
+    a row with no key gets O = 0 and LSE = sink).  Returns out [Hq,total_q,D]
+    and lse [Hq,total_q].
+    """
+    Hq, total_q, D = q.shape
+    out = np.zeros((Hq, total_q, D))
+    lse = np.zeros((Hq, total_q))
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        if q1 <= q0:
+            continue
+        o, l = attention_fwd(np.asarray(q)[None, :, q0:q1], np.asarray(k)[None, :, k0:k1],
+                             np.asarray(v)[None, :, k0:k1], sinks, window, scale)
+        out[:, q0:q1] = o[0]
+        lse[:, q0:q1] = l[0]
     return out, lse
 
 

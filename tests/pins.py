@@ -320,3 +320,92 @@ def err_plan(seed=0, B=40, Lk_max=5000, window=0, Hq=64, Hkv=8, max_splits=64, s
     want = brute_plan_auto(seqlens, Hq, Hkv, Lk_max, window, max_splits, slots)
     bad += sum(g != w for g, w in zip(got, want))
     return bad
+
+
+# --- paged KV and varlen ---------------------------------------------------------
+
+def make_paged(dense, seqlens, page_size, seed, extra_pages=3):
+    """Scatter a dense cache [B,Hkv,Lk_max,D] into pages in a random order.
+
+    Returns pages [num_pages,Hkv,page_size,D] (unused pages and rows NaN) and
+    a block table [B,max_pages] whose unused slots name a NaN page."""
+    rng = np.random.default_rng(seed)
+    B, Hkv, Lk_max, D = dense.shape
+    max_pages = -(-Lk_max // page_size)
+    need = [-(-int(L) // page_size) for L in seqlens]
+    num_pages = sum(need) + extra_pages
+    order = rng.permutation(num_pages)
+    pages = np.full((num_pages, Hkv, page_size, D), np.nan)
+    table = np.full((B, max_pages), int(order[-1]), dtype=np.int64)  # a NaN page
+    k = 0
+    for b in range(B):
+        for p in range(need[b]):
+            pid = int(order[k]); k += 1
+            table[b, p] = pid
+            rows = dense[b, :, p * page_size:(p + 1) * page_size]
+            pages[pid, :, :rows.shape[1]] = rows
+    return pages, table
+
+
+def err_paged(seed=0, B=5, Hq=4, Hkv=2, Lk_max=300, D=8, page_size=16, window=0):
+    """Paged decode through a shuffled block table equals the dense decode."""
+    rng = np.random.default_rng(seed)
+    seqlens = rng.integers(1, Lk_max + 1, B)
+    q = rand((B, Hq, 1, D), seed)
+    kc, vc = rand((B, Hkv, Lk_max, D), seed + 1), rand((B, Hkv, Lk_max, D), seed + 2)
+    sinks = rand(Hq, seed + 3)
+    kp, table = make_paged(kc, seqlens, page_size, seed)
+    vp, table2 = make_paged(vc, seqlens, page_size, seed)
+    assert np.array_equal(table, table2)
+    o, l = oracle.decode_paged(q, kp, vp, table, seqlens, sinks, window, 0.4, page_size, Lk_max)
+    od, ld = oracle.decode(q, kc, vc, seqlens, sinks, window, 0.4)
+    # key by key through the table, by hand
+    worst = max(np.abs(o - od).max(), np.abs(l - ld).max())
+    g = oracle.gather_paged(kp, table, seqlens, page_size, Lk_max)
+    for b in range(B):
+        for j in range(int(seqlens[b])):
+            pid = table[b, j // page_size]
+            worst = max(worst, np.abs(g[b, :, j] - kp[pid, :, j % page_size]).max())
+        assert np.isnan(g[b, :, int(seqlens[b]):]).all()
+    return worst
+
+
+def err_varlen_equal_lengths(seed=0, B=3, Hq=4, Hkv=2, L=40, D=8, window=7):
+    """Equal lengths: the packed batch equals the dense batched call."""
+    q, k, v = rand((B, Hq, L, D), seed), rand((B, Hkv, L, D), seed + 1), rand((B, Hkv, L, D), seed + 2)
+    sinks = rand(Hq, seed + 3)
+    o, l = oracle.attention_fwd(q, k, v, sinks, window, 0.3)
+    pack = lambda x: np.concatenate(list(x), axis=1)  # [B,H,L,D] -> [H,B*L,D]
+    cu = np.arange(B + 1) * L
+    ov, lv = oracle.attention_fwd_varlen(pack(q), pack(k), pack(v), cu, cu, sinks, window, 0.3)
+    return max(np.abs(ov - pack(o)).max(), np.abs(lv - np.concatenate(list(l), axis=1)).max())
+
+
+def err_varlen_brute(seed=0, Hq=2, Hkv=1, D=3, window=3):
+    """Mixed lengths (Lq < Lk, Lq > Lk, empty) against brute force per sequence."""
+    lq = [3, 1, 0, 4, 5]
+    lk = [5, 1, 2, 4, 2]
+    cu_q = np.concatenate([[0], np.cumsum(lq)])
+    cu_k = np.concatenate([[0], np.cumsum(lk)])
+    q = rand((Hq, cu_q[-1], D), seed)
+    k, v = rand((Hkv, cu_k[-1], D), seed + 1), rand((Hkv, cu_k[-1], D), seed + 2)
+    sinks = rand(Hq, seed + 3)
+    o, l = oracle.attention_fwd_varlen(q, k, v, cu_q, cu_k, sinks, window, 0.7)
+    worst = 0.0
+    for b in range(len(lq)):
+        if lq[b] == 0:
+            continue
+        qs = q[None, :, cu_q[b]:cu_q[b + 1]]
+        ks, vs = k[None, :, cu_k[b]:cu_k[b + 1]], v[None, :, cu_k[b]:cu_k[b + 1]]
+        if lq[b] <= lk[b]:
+            ob, lb = brute_force(qs, ks, vs, sinks, window, 0.7)
+        else:
+            # queries past the keys: the first lq-lk rows see nothing
+            pad = lq[b] - lk[b]
+            ob = np.zeros((1, Hq, lq[b], D))
+            lb = np.broadcast_to(np.asarray(sinks, np.float64)[None, :, None], (1, Hq, lq[b])).copy()
+            o2, l2 = brute_force(qs[:, :, pad:], ks, vs, sinks, window, 0.7)
+            ob[:, :, pad:], lb[:, :, pad:] = o2, l2
+        worst = max(worst, np.abs(o[:, cu_q[b]:cu_q[b + 1]] - ob[0]).max(),
+                    np.abs(l[:, cu_q[b]:cu_q[b + 1]] - lb[0]).max())
+    return worst

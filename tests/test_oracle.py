@@ -422,3 +422,37 @@ def test_plan_pins_catch_changed_rule(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(oa, "PLAN_CHUNKS", (512, 1024, 2048))
         assert pins.err_plan(1, 64, 32768) > 0
+
+
+# --- paged KV and varlen -------------------------------------------------------------
+
+@pytest.mark.parametrize("page_size,window", [(16, 0), (1, 0), (64, 100), (7, 5)])
+def test_paged_decode_equals_dense(page_size, window):
+    assert pins.err_paged(page_size=page_size, window=window) < 1e-12
+
+
+def test_varlen_equal_lengths_is_dense_batch():
+    assert pins.err_varlen_equal_lengths() < 1e-12
+    assert pins.err_varlen_equal_lengths(window=0, L=33) < 1e-12
+
+
+@pytest.mark.parametrize("window", [0, 2, 3])
+def test_varlen_brute_force(window):
+    assert pins.err_varlen_brute(window=window) < 1e-12
+
+
+def test_paged_varlen_pins_catch_mistakes(monkeypatch):
+    with monkeypatch.context() as m:   # row within the page off by one
+        m.setattr(oa, "page_slot", lambda j, ps: (j // ps, (j + 1) % ps))
+        assert pins.err_paged(page_size=4, Lk_max=12) > 1e-6
+    orig = oa.attention_fwd
+
+    def global_positions(q, k, v, sinks, window, scale, block=256):
+        # a mistake: every sequence aligned top-left instead of bottom-right
+        Lq, Lk = q.shape[2], k.shape[2]
+        if Lq < Lk:
+            k, v = k[:, :, :Lq], v[:, :, :Lq]
+        return orig(q, k, v, sinks, window, scale, block)
+    with monkeypatch.context() as m:
+        m.setattr(oa, "attention_fwd", global_positions)
+        assert pins.err_varlen_brute(window=3) > 1e-6
