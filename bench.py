@@ -146,6 +146,78 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
     return rows
 
 
+def pairs_window(L: int, W: int) -> int:
+    """Unmasked (query, key) pairs of one head: sum_i min(i + 1, W) (W <= 0: causal)."""
+    if W <= 0 or W >= L:
+        return L * (L + 1) // 2
+    return W * (W + 1) // 2 + (L - W) * W
+
+
+def measure_serving(A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
+                    dense_s, wp, reps=20):
+    """Paged decode (pages shuffled) against the dense decode on the same cache,
+    and the varlen forward on a packed batch, each timed with events on stream."""
+    def timeit(fn):
+        with torch.cuda.stream(stream):
+            for _ in range(5):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    res = {"paged_decode": [], "varlen_prefill": None}
+    nbytes = decode_bytes(seqlens, wd.Hq, wd.Hkv, wd.D, wd.window)
+    res["paged_decode"].append({"layout": "dense", "us": round(dense_s * 1e6, 1),
+                                "GB/s": round(nbytes / dense_s / 1e9, 1)})
+    B, Hkv, Lk_max, D = kd.shape
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    for ps in (16, 256):
+        npp = Lk_max // ps
+        perm = torch.randperm(B * npp, device=dev, generator=g)
+        inv = torch.empty_like(perm)
+        inv[perm] = torch.arange(B * npp, device=dev)
+        table = inv.view(B, npp).to(torch.int32).contiguous()   # page of (b, slot)
+
+        def paged(x):
+            ordered = x.view(B, Hkv, npp, ps, D).permute(0, 2, 1, 3, 4).reshape(B * npp, Hkv, ps, D)
+            return ordered[perm].contiguous()
+        kp, vp = paged(kd), paged(vd)
+
+        def step():
+            A.attn_decode_splitkv_paged(qd, kp, vp, table, sl, ns, op, lp, window=wd.window,
+                                        scale=wd.scale, stream=stream)
+            A.attn_combine(op, lp, sl, ns, ds, dout, dlse, Lk_max=npp * ps, window=wd.window,
+                           stream=stream)
+        t = timeit(step)
+        res["paged_decode"].append({"layout": f"paged {ps}", "us": round(t * 1e6, 1),
+                                    "GB/s": round(nbytes / t / 1e9, 1)})
+        del kp, vp
+        torch.cuda.empty_cache()
+
+    # packed batch: 8 sequences of U{1024..8192} rows, the sliding-window prefill's heads
+    lens = np.random.default_rng(11).integers(1024, 8193, 8)
+    tot = int(lens.sum())
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    q = torch.randn(wp.Hq, tot, wp.D, device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn(wp.Hkv, tot, wp.D, device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn(wp.Hkv, tot, wp.D, device=dev, generator=g).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lse = torch.empty(wp.Hq, tot, device=dev)
+    t = timeit(lambda: A.attn_fwd_varlen(q, k, v, cu, cu, None, out, lse,
+                                         max_seqlen_q=int(lens.max()), window=wp.window,
+                                         scale=wp.scale, stream=stream))
+    flops = 4 * wp.D * wp.Hq * sum(pairs_window(int(L), wp.window) for L in lens)
+    res["varlen_prefill"] = {"workload": f"8 sequences, lengths {sorted(int(x) for x in lens)}, "
+                                         f"Hq{wp.Hq} Hkv{wp.Hkv} D{wp.D} window{wp.window}",
+                             "ms": round(t * 1e3, 4), "TFLOP/s": round(flops / t / 1e12, 2)}
+    return res
+
+
 def cpu_baseline(w, q, k, v, sinks, budget_s=20.0):
     """Time the float64 oracle on whole heads of the prefill until ~budget_s of work."""
     import oracle
@@ -178,6 +250,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the step (no split-policy, serving or max-logit extras); "
+                         "the profiled runs use this so that every kernel's dispatches are the step's")
     ap.add_argument("--prefill", default="swa_prefill",
                     help="prefill workload (swa_prefill is the headline; others for study)")
     ap.add_argument("--keys-per-split", type=int, default=0,
@@ -259,27 +334,40 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
+    timed = ev[args.warmup:]
+    t_fwd = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e-3
+    t_dec = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e-3
+    t_cmb = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e-3
+
     # Split-count policies (attn_decode_plan): decode + combine GB/s with the
     # workload-aware plan (the plan kernel inside the timed span) against
     # fixed rules, on the decode workload above and two more batch/length mixes.
-    split_policy = measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp,
-                                          dout, dlse, wd, seqlens)
+    split_policy = None if args.step_only else measure_split_policies(
+        A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd, seqlens)
 
-    # attn_fwd_max_logit (per-row and per-head maxima) on the same prefill,
-    # timed like attn_fwd, to report what the extra outputs cost.
-    ml_row = torch.empty(lse.shape, dtype=torch.float32, device=dev)
-    ml_head = torch.empty(lse.shape[:2], dtype=torch.float32, device=dev)
-    n_ml = max(10, args.steps // 5)
-    ml_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(n_ml)]
-    with torch.cuda.stream(stream):
-        for e0, e1 in ml_ev:
-            e0.record(stream)
-            A.attn_fwd_max_logit(q, k, v, s, out, lse, ml_row, ml_head, window=wp.window,
-                                 scale=wp.scale, stream=stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-    t_ml = np.array([e0.elapsed_time(e1) for e0, e1 in ml_ev[n_ml // 2:]]) * 1e-3
+    # Serving layouts: decode over a shuffled paged copy of the same cache, and
+    # the forward over a packed batch of sequences of different lengths.
+    serving = None if args.step_only else measure_serving(
+        A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
+        t_dec.mean() + t_cmb.mean(), wp)
+
+    t_ml = None
+    if not args.step_only:
+        # attn_fwd_max_logit (per-row and per-head maxima) on the same prefill,
+        # timed like attn_fwd, to report what the extra outputs cost.
+        ml_row = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+        ml_head = torch.empty(lse.shape[:2], dtype=torch.float32, device=dev)
+        n_ml = max(10, args.steps // 5)
+        ml_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(n_ml)]
+        with torch.cuda.stream(stream):
+            for e0, e1 in ml_ev:
+                e0.record(stream)
+                A.attn_fwd_max_logit(q, k, v, s, out, lse, ml_row, ml_head, window=wp.window,
+                                     scale=wp.scale, stream=stream)
+                e1.record(stream)
+            torch.cuda.synchronize()
+        t_ml = np.array([e0.elapsed_time(e1) for e0, e1 in ml_ev[n_ml // 2:]]) * 1e-3
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -290,17 +378,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    timed = ev[args.warmup:]
-    t_fwd = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e-3
-    t_dec = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e-3
-    t_cmb = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e-3
 
     flops = wp.flops()
     tflops = flops / t_fwd.mean() / 1e12
     dbytes = decode_bytes(seqlens, wd.Hq, wd.Hkv, wd.D, wd.window)
     dec_gbps = dbytes / (t_dec.mean() + t_cmb.mean()) / 1e9
-    traffic = stored_traffic("fwd_bf16_kernel<128,false,false>:" + wp.name)
-    dec_traffic = stored_traffic("decode_kernel<128>:" + wd.name)
+    traffic = stored_traffic("fwd_bf16_kernel<128,false,false,false>:" + wp.name)
+    dec_traffic = stored_traffic("decode_kernel<128,false>:" + wd.name)
     dec_only = dbytes / t_dec.mean() / 1e9
 
     res = {
@@ -331,7 +415,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "fwd_bf16_kernel<128,false,false>",
+            "kernel": "fwd_bf16_kernel<128,false,false,false>",
             "ms_per_launch": round(t_fwd.mean() * 1e3, 4),
         },
         "decode": {
@@ -348,17 +432,19 @@ def main():
             "unit": "GB/s",
             "frac": round(dec_only / PEAK_HBM_GBPS, 4),
             "traffic": dec_traffic,
-            "kernel": "decode_kernel<128>",
+            "kernel": "decode_kernel<128,false>",
             "ms_per_launch": round(t_dec.mean() * 1e3, 4),
         },
     }
-    res["split_policy"] = split_policy
-    res["max_logit"] = {
-        "entry": "attn_fwd_max_logit (row [B,Hq,Lq] and head [B,Hq] maxima)",
-        "ms_per_launch": round(t_ml.mean() * 1e3, 4),
-        "TFLOP/s": round(flops / t_ml.mean() / 1e12, 2),
-        "time_vs_attn_fwd": round(t_ml.mean() / t_fwd.mean(), 4),
-    }
+    if not args.step_only:
+        res["split_policy"] = split_policy
+        res["serving"] = serving
+        res["max_logit"] = {
+            "entry": "attn_fwd_max_logit (row [B,Hq,Lq] and head [B,Hq] maxima)",
+            "ms_per_launch": round(t_ml.mean() * 1e3, 4),
+            "TFLOP/s": round(flops / t_ml.mean() / 1e12, 2),
+            "time_vs_attn_fwd": round(t_ml.mean() / t_fwd.mean(), 4),
+        }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wp, qh, kh, vh, sh)
     print(json.dumps(res), flush=True)

@@ -13,7 +13,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_decode_plan", "attn_combine", "attn_strerror", "AttnError",
+__all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_decode_splitkv",
+           "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine", "attn_strerror", "AttnError",
            "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
 
 ATTN_BF16 = 0
@@ -36,6 +37,8 @@ _SIGNATURES = {
     "attn_decode_splitkv": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp],
     "attn_combine": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "attn_decode_plan": [_vp, _vp] + [_i] * 8 + [_vp],
+    "attn_fwd_varlen": [_vp] * 8 + [_i] * 8 + [_f, _i, _i, _vp],
+    "attn_decode_splitkv_paged": [_vp] * 8 + [_i] * 9 + [_f, _i, _vp],
     "attn_strerror": [_i],
     "attn_version": [],
 }
@@ -171,6 +174,65 @@ def attn_fwd_max_logit(q, k, v, sinks, out, lse=None, max_row=None, max_head=Non
         B, Hq, Hkv, Lq, Lk, D, int(window), float(scale), _dtype_code(q), _dtype_code(out),
         _stream(stream))
     _check("attn_fwd_max_logit", rc)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, out, lse=None, *,
+                    max_seqlen_q: int, window: int = 0, scale: float | None = None,
+                    stream=None) -> None:
+    """attn_fwd over a packed batch: q [Hq,total_q,D], k/v [Hkv,total_k,D] (bf16),
+    cu_seqlens_q/k [B+1] int32 (device), out [Hq,total_q,D], lse [Hq,total_q] or None."""
+    import torch
+
+    Hq, total_q, D = q.shape
+    Hkv, total_k, _ = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if tuple(cu_seqlens_k.shape) != (B + 1,):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    if tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/k/v/out")
+    if sinks is not None and tuple(sinks.shape) != (Hq,):
+        raise ValueError("sinks must be [Hq]")
+    if lse is not None and tuple(lse.shape) != (Hq, total_q):
+        raise ValueError("lse must be [Hq,total_q]")
+    if scale is None:
+        scale = D ** -0.5
+    rc = load_library().attn_fwd_varlen(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), _dev(sinks, "sinks", torch.float32),
+        _dev(out, "out"), _dev(lse, "lse", torch.float32), B, Hq, Hkv, total_q, total_k,
+        int(max_seqlen_q), D, int(window), float(scale), _dtype_code(q), _dtype_code(out),
+        _stream(stream))
+    _check("attn_fwd_varlen", rc)
+
+
+def attn_decode_splitkv_paged(q, k_pages, v_pages, block_table, seqlens_k, num_splits, o_part,
+                              lse_part, *, window: int = 0, scale: float | None = None,
+                              stream=None) -> None:
+    """attn_decode_splitkv over a paged cache: pages [num_pages,Hkv,page_size,D] bf16,
+    block_table [B,max_pages] int32.  Pass Lk_max = max_pages * page_size to attn_combine."""
+    import torch
+
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query per sequence: q must be [B,Hq,1,D]")
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    max_splits = o_part.shape[2]
+    if tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages and v_pages shapes differ")
+    if tuple(block_table.shape) != (B, max_pages):
+        raise ValueError("block_table must be [B,max_pages]")
+    if tuple(o_part.shape) != (B, Hq, max_splits, D) or tuple(lse_part.shape) != (B, Hq, max_splits):
+        raise ValueError("o_part must be [B,Hq,max_splits,D] and lse_part [B,Hq,max_splits]")
+    if scale is None:
+        scale = D ** -0.5
+    rc = load_library().attn_decode_splitkv_paged(
+        _dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+        _dev(block_table, "block_table", torch.int32), _dev(seqlens_k, "seqlens_k", torch.int32),
+        _dev(num_splits, "num_splits", torch.int32), _dev(o_part, "o_part", torch.float32),
+        _dev(lse_part, "lse_part", torch.float32), B, Hq, Hkv, num_pages, page_size, max_pages, D,
+        max_splits, int(window), float(scale), _dtype_code(q), _stream(stream))
+    _check("attn_decode_splitkv_paged", rc)
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_part, *,

@@ -80,6 +80,32 @@ int attn_fwd_max_logit(const void* q, const void* k, const void* v, const float*
                                    out_dtype == ATTN_F32, static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, const float* sinks, void* out, float* lse, int B,
+                    int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int D, int window,
+                    float scale, int in_dtype, int out_dtype, void* stream) {
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || total_k < 0 || max_seqlen_q < 1)
+    return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || B > 65535 || max_seqlen_q > total_q) return ATTN_ERR_SHAPE;
+  if (!fits(Hq, total_q, D, 1) || !fits(Hkv, total_k, D, 1) || !fits(B, Hq, 1, 1))
+    return ATTN_ERR_SHAPE;
+  if ((long long)((max_seqlen_q + 31) / 32) * Hq * B >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if ((long long)total_k * D * 4 >= (1LL << 32) || (long long)Hq * total_q >= (1LL << 31) ||
+      (long long)Hkv * total_k >= (1LL << 31))
+    return ATTN_ERR_SHAPE;
+  if (!supported_dim(D) || in_dtype != ATTN_BF16 || !dtype_ok(out_dtype)) return ATTN_ERR_UNSUPPORTED;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return ATTN_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_VALUE;
+  for (const void* p : {(const void*)cu_seqlens_q, (const void*)cu_seqlens_k, (const void*)lse,
+                        (const void*)sinks})
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return ATTN_ERR_VALUE;
+  return from_hip(attn::launch_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, out, lse, B,
+                                          Hq, Hkv, total_q, total_k, max_seqlen_q, D, window,
+                                          scale, out_dtype == ATTN_F32,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
                         float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
@@ -99,6 +125,39 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   return from_hip(attn::launch_decode(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_part,
                                       B, Hq, Hkv, Lk_max, D, max_splits, window, scale,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int attn_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* seqlens_k,
+                              const int32_t* num_splits, float* o_part, float* lse_part, int B,
+                              int Hq, int Hkv, int num_pages, int page_size, int max_pages_per_seq,
+                              int D, int max_splits, int window, float scale, int in_dtype,
+                              void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seqlens_k || !num_splits || !o_part ||
+      !lse_part)
+    return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || num_pages < 1 || page_size < 1 || max_pages_per_seq < 1)
+    return ATTN_ERR_SHAPE;
+  if ((page_size & (page_size - 1)) != 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || max_splits < 1 || max_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
+  const long long Lk_max = (long long)max_pages_per_seq * page_size;
+  if (Lk_max >= (1LL << 31) || !fits(num_pages, Hkv, page_size, D) || !fits(B, Hq, max_splits, D) ||
+      !fits(B, max_pages_per_seq, 1, 1))
+    return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq >= (1LL << 31) || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+  if (!supported_dim(D) || in_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return ATTN_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o_part) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u) || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) ||
+      (reinterpret_cast<uintptr_t>(num_splits) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return ATTN_ERR_VALUE;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  return from_hip(attn::launch_decode_paged(q, k_pages, v_pages, block_table, seqlens_k,
+                                            num_splits, o_part, lse_part, B, Hq, Hkv, (int)Lk_max,
+                                            num_pages, shift, max_pages_per_seq, D, max_splits,
+                                            window, scale, static_cast<hipStream_t>(stream)));
 }
 
 int attn_decode_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int Hq, int Hkv,

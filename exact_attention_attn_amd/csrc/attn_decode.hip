@@ -33,13 +33,15 @@ constexpr float kRebaseThreshold = 8.0f;
 
 struct DecArgs {
   const uint16_t* q;
-  const uint16_t* k;
+  const uint16_t* k;  // [B,Hkv,Lk_max,D], or pages [num_pages,Hkv,page_size,D]
   const uint16_t* v;
   const int32_t* seqlens;
   const int32_t* nsplits;
+  const int32_t* table;  // paged: block table [B, max_pages]
   float* o_part;
   float* lse_part;
   int B, Hq, Hkv, Lk_max, max_splits, window, n_qgroups;
+  int max_pages, page_shift, num_pages;  // paged: page_size = 1 << page_shift
   float c;  // scale * log2(e)
 };
 
@@ -78,7 +80,10 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // Persistent split-KV decode: work-group w of n streams items
 // [total*w/n, total*(w+1)/n) of the flat item list; the copy of the next tile
 // (possibly the next item's first) is in flight while a tile is computed.
-template <int D>
+// PAGED: key j of sequence b is row j % page_size of page
+// table[b][j / page_size]; each lane looks up the pages of its rows (page ids
+// are clamped into the pool, so a bad table cannot address outside it).
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   using Tile = BfTile<D>;
   constexpr int TILE_BYTES = kTileKeys * Tile::kRowBytes;
@@ -152,19 +157,56 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
     return p + ((size_t)(x.b * a.Hkv + x.kvh) * a.Lk_max) * D;
   };
   u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](const Item& x, int t0) {
-    const uint16_t* kh = kv_base(x, a.k);
-    const uint16_t* vh = kv_base(x, a.v);
+  // PAGED: page ids of the rows of the tile that load_tile fetches next.  They
+  // are loaded one tile ahead, so the table's latency does not delay the K/V
+  // loads that depend on it.
+  int pid_next[PAGED ? LOADS : 1];
+  auto lookup_pages = [&](const Item& x, int t0) {
+    if constexpr (PAGED) {
+      const int32_t* tb = a.table + (size_t)x.b * a.max_pages;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int cid = threadIdx.x + i * kThreads;
-      int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
-      // Rows past the split are loaded from its last key: they are masked
-      // (p = 0) and finite, so they add nothing.  Rows >= Lk are never read.
-      // Each cache byte is read once: non-temporal loads keep it out of the caches.
-      int key = min(t0 + r, x.k_end - 1);
-      kreg[i] = __builtin_nontemporal_load((const u32x4*)(kh + (size_t)key * D + cch * 8));
-      vreg[i] = __builtin_nontemporal_load((const u32x4*)(vh + (size_t)key * D + cch * 8));
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = (threadIdx.x + i * kThreads) / Tile::kChunks;
+        pid_next[i] = tb[min(t0 + r, x.k_end - 1) >> a.page_shift];
+      }
+    }
+  };
+  // The item after the cursor, leaving the cursor where it is.
+  auto peek = [&]() {
+    const int b = cur_b, r = cur_r, n = cur_n;
+    const SplitRange sr = cur_sr;
+    const Item nxt = advance();
+    cur_b = b; cur_r = r; cur_n = n; cur_sr = sr;
+    return nxt;
+  };
+  auto load_tile = [&](const Item& x, int t0) {
+    // Rows past the split are loaded from its last key: they are masked
+    // (p = 0) and finite, so they add nothing.  Rows >= Lk are never read.
+    // Each cache byte is read once: non-temporal loads keep it out of the caches.
+    if constexpr (PAGED) {
+      // page ids were looked up one tile earlier (lookup_pages)
+      const int mask = (1 << a.page_shift) - 1;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        int cid = threadIdx.x + i * kThreads;
+        int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
+        int key = min(t0 + r, x.k_end - 1);
+        const int pg = min(max(pid_next[i], 0), a.num_pages - 1);
+        const size_t row = (((size_t)pg * a.Hkv + x.kvh) << a.page_shift) + (key & mask);
+        kreg[i] = __builtin_nontemporal_load((const u32x4*)(a.k + row * D + cch * 8));
+        vreg[i] = __builtin_nontemporal_load((const u32x4*)(a.v + row * D + cch * 8));
+      }
+    } else {
+      const uint16_t* kh = kv_base(x, a.k);
+      const uint16_t* vh = kv_base(x, a.v);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        int cid = threadIdx.x + i * kThreads;
+        int r = cid / Tile::kChunks, cch = cid % Tile::kChunks;
+        int key = min(t0 + r, x.k_end - 1);
+        kreg[i] = __builtin_nontemporal_load((const u32x4*)(kh + (size_t)key * D + cch * 8));
+        vreg[i] = __builtin_nontemporal_load((const u32x4*)(vh + (size_t)key * D + cch * 8));
+      }
     }
   };
   auto store_tile = [&]() {
@@ -200,7 +242,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
 
   int t0 = it.k_begin;
   load_q(it);
-  load_tile(it, t0);
+  if constexpr (PAGED) {
+    lookup_pages(it, t0);
+    load_tile(it, t0);
+    if (t0 + kTileKeys < it.k_end) lookup_pages(it, t0 + kTileKeys);
+    else if (items_left > 1) { const Item nn = peek(); lookup_pages(nn, nn.k_begin); }
+  } else {
+    load_tile(it, t0);
+  }
   while (true) {
     __syncthreads();  // every wave is done with the previous tile
     store_tile();
@@ -220,6 +269,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
       nt0 = nx.k_begin;
     }
     if (has_next) load_tile(nx, nt0);
+    if constexpr (PAGED) {
+      // page ids of the tile after (nx, nt0): later in nx, or the first of
+      // the item after it (items_left counts the current item)
+      if (has_next) {
+        if (nt0 + kTileKeys < nx.k_end) {
+          lookup_pages(nx, nt0 + kTileKeys);
+        } else if (items_left - (last ? 2 : 1) > 0) {
+          const Item nn = peek();
+          lookup_pages(nn, nn.k_begin);
+        }
+      }
+    }
     __syncthreads();
 
     const int w0 = t0 + wave * kKeysPerWave;
@@ -516,9 +577,20 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
                          const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
                          float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
                          int max_splits, int window, float scale, hipStream_t stream) {
+  return launch_decode_paged(q, k_cache, v_cache, nullptr, seqlens_k, num_splits, o_part, lse_part,
+                             B, Hq, Hkv, Lk_max, 0, 0, 0, D, max_splits, window, scale, stream);
+}
+
+hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seqlens_k,
+                               const int32_t* num_splits, float* o_part, float* lse_part, int B,
+                               int Hq, int Hkv, int Lk_max, int num_pages, int page_shift,
+                               int max_pages, int D, int max_splits, int window, float scale,
+                               hipStream_t stream) {
   DecArgs a;
-  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k_cache; a.v = (const uint16_t*)v_cache;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k_pages; a.v = (const uint16_t*)v_pages;
   a.seqlens = seqlens_k; a.nsplits = num_splits; a.o_part = o_part; a.lse_part = lse_part;
+  a.table = block_table; a.num_pages = num_pages; a.page_shift = page_shift; a.max_pages = max_pages;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lk_max = Lk_max; a.max_splits = max_splits; a.window = window;
   int G = Hq / Hkv;
   a.n_qgroups = (G + 31) / 32;
@@ -526,10 +598,14 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
   // Persistent grid: two work-groups per compute unit, each streaming a
   // contiguous range of the item list.
   dim3 grid(2 * cu_count());
-  if (D == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+  const bool paged = block_table != nullptr;
+  if (D == 128) {
+    if (paged) hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (paged) hipLaunchKernelGGL((decode_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

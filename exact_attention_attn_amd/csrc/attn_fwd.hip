@@ -131,7 +131,10 @@ struct FwdArgs {
   float* lse;
   float* max_row;   // [B,Hq,Lq] largest pre-softmax logit per row, or NULL
   float* max_head;  // [B,Hq] largest per head (filled with -inf beforehand), or NULL
-  int B, Hq, Hkv, Lq, Lk, window;
+  const int32_t* cu_q;  // packed batch: [B+1] row offsets of the sequences
+  const int32_t* cu_k;  // packed batch: [B+1] key offsets
+  int total_q, total_k;
+  int B, Hq, Hkv, Lq, Lk, window;  // packed batch: Lq = the longest sequence
   float c;      // scale * log2(e)
   float scale;  // softmax scale (the logit is scale * <q, k>)
   int n_qtiles;
@@ -393,9 +396,22 @@ struct BfSmem {
 struct BfWork {
   int b, kvh, hg, qt;
 };
+// A packed batch mixes long and short sequences, and contiguous ranges per XCD
+// would leave the XCDs that hold the long ones with most of the work: there
+// the groups (b, kvh, hg) are dealt round-robin over the XCDs instead (each
+// XCD still runs whole groups, so their K/V tiles stay in its L2).
+template <bool VARLEN>
 __device__ __forceinline__ BfWork decode_bf_work(const FwdArgs& a, int n_hg) {
-  int total = a.n_qtiles * n_hg * a.Hkv * a.B;
-  int id = xcd_remap(blockIdx.x, total);
+  constexpr int kXcd = 8;
+  const int n_groups = n_hg * a.Hkv * a.B;
+  const int total = a.n_qtiles * n_groups;
+  int id;
+  if (VARLEN && n_groups % kXcd == 0) {
+    const int xcd = blockIdx.x % kXcd, k = blockIdx.x / kXcd;  // k-th work-group of this XCD
+    id = ((k / a.n_qtiles) * kXcd + xcd) * a.n_qtiles + k % a.n_qtiles;
+  } else {
+    id = xcd_remap(blockIdx.x, total);
+  }
   BfWork w;
   w.qt = a.n_qtiles - 1 - id % a.n_qtiles;
   id /= a.n_qtiles;
@@ -412,7 +428,10 @@ __host__ __device__ __forceinline__ int bf_heads_per_group(int G) {
   return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
-template <int D, bool OUT_F32, bool MAXL>
+// VARLEN: a packed batch (q [Hq,total_q,D], k/v [Hkv,total_k,D]); sequence b
+// owns rows cu_q[b].. and keys cu_k[b].., and a work-group whose q-tile lies
+// past its sequence's rows leaves at once.
+template <int D, bool OUT_F32, bool MAXL, bool VARLEN>
 __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using L = BfLayout<D>;
   using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
@@ -424,23 +443,39 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int G = a.Hq / a.Hkv;
   const int HG = bf_heads_per_group(G);
   const int rows = kBfWaves / HG * kRowsPerWave;  // query rows per work-group
-  const BfWork wk = decode_bf_work(a, G / HG);
+  const BfWork wk = decode_bf_work<VARLEN>(a, G / HG);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int off_q = a.Lk - a.Lq;
   const int h = wk.kvh * G + wk.hg * HG + wave % HG;  // this wave's query head
 
-  const uint16_t* qh = (const uint16_t*)a.q + ((size_t)(wk.b * a.Hq + h) * a.Lq) * D;
-  const uint16_t* kh = (const uint16_t*)a.k + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
-  const uint16_t* vh = (const uint16_t*)a.v + ((size_t)(wk.b * a.Hkv + wk.kvh) * a.Lk) * D;
+  // Rows and keys of this (batch, head): dense [B,H,L,D], or one sequence of
+  // a packed batch (offsets clamped into the packed tensors).
+  int Lq = a.Lq, Lk = a.Lk;
+  size_t q_row0, k_row0;  // first row of this (sequence, head) in q/out and in k/v
+  if constexpr (VARLEN) {
+    const int q0 = min(max(a.cu_q[wk.b], 0), a.total_q);
+    const int k0 = min(max(a.cu_k[wk.b], 0), a.total_k);
+    Lq = min(max(a.cu_q[wk.b + 1], q0), a.total_q) - q0;
+    Lk = min(max(a.cu_k[wk.b + 1], k0), a.total_k) - k0;
+    if (wk.qt * rows >= Lq) return;  // uniform: no barrier has been reached
+    q_row0 = (size_t)h * a.total_q + q0;
+    k_row0 = (size_t)wk.kvh * a.total_k + k0;
+  } else {
+    q_row0 = (size_t)(wk.b * a.Hq + h) * Lq;
+    k_row0 = (size_t)(wk.b * a.Hkv + wk.kvh) * Lk;
+  }
+  const int off_q = Lk - Lq;
+  const uint16_t* qh = (const uint16_t*)a.q + q_row0 * D;
+  const uint16_t* kh = (const uint16_t*)a.k + k_row0 * D;
+  const uint16_t* vh = (const uint16_t*)a.v + k_row0 * D;
 
   const int r0 = wk.qt * rows;
-  const int r_end = min(r0 + rows, a.Lq);
+  const int r_end = min(r0 + rows, Lq);
   const RowSpan wg_span = {r0 + off_q, r_end - 1 + off_q};
   const int w0 = r0 + (wave / HG) * kRowsPerWave;
-  const bool wave_active = w0 < a.Lq;
-  const RowSpan w_span = {w0 + off_q, min(w0 + kRowsPerWave, a.Lq) - 1 + off_q};
+  const bool wave_active = w0 < Lq;
+  const RowSpan w_span = {w0 + off_q, min(w0 + kRowsPerWave, Lq) - 1 + off_q};
   const int key_lo = a.window > 0 ? max(0, wg_span.p_first - a.window + 1) : 0;
   const int key_hi = wg_span.p_last + 1;
   const int t_begin = key_lo / kBc, t_end = (key_hi + kBc - 1) / kBc;
@@ -448,11 +483,11 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Two-stage ring: tile t lives in stage (t - t_begin) % 2.
   TileCopy<D> cp;
   cp.init(wave, lane);
-  cp.issue(kh, vh, t_begin, a.Lk, K0, V0);
+  if (t_begin < t_end) cp.issue(kh, vh, t_begin, Lk, K0, V0);  // no tile: no key visible
 
   // Q^T operand: lane holds query row w0+col, d = ks*16 + half*8 .. +8.
   const int my_row = w0 + col;
-  const bool row_valid = my_row < a.Lq;
+  const bool row_valid = my_row < Lq;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -465,8 +500,12 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
   Row row = {kNegInf, 0.0f, kNegInf};
   const int p = my_row + off_q;
-  const int vis_hi = min(p, a.Lk - 1);
-  const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
+  int vis_hi = min(p, Lk - 1);
+  int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
+  // A row before every key (p < 0: more queries than keys in a packed batch)
+  // sees nothing; an empty range would wrap in the unsigned mask compare, so
+  // it is moved far past every key instead.
+  if (vis_hi < vis_lo) vis_lo = vis_hi = 1 << 30;
 
   // Per-lane operand read addresses within a stage.  K: row key_perm(col),
   // chunk ks*2 + half.  V (transposed reads): keys half*8 + (lane%16)/4 + 4e,
@@ -487,8 +526,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   auto step = [&](int t, const lds_char* ks_, const lds_char* vs_, lds_char* kn, lds_char* vn) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (t + 1 < t_end) cp.issue(kh, vh, t + 1, a.Lk, kn, vn);
-    const int kind = wave_active ? tile_kind(t * kBc, kBc, w_span, a.window, a.Lk) : 0;
+    if (t + 1 < t_end) cp.issue(kh, vh, t + 1, Lk, kn, vn);
+    const int kind = wave_active ? tile_kind(t * kBc, kBc, w_span, a.window, Lk) : 0;
     if (kind != 0)
       bf16_tile<D, MAXL>(ks_, vs_, ka, va, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
   };
@@ -499,8 +538,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   const float sink_l2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-  OutT* orow = (OutT*)a.out + ((size_t)(wk.b * a.Hq + h) * a.Lq + my_row) * D;
-  float* lse_dst = a.lse ? a.lse + (size_t)(wk.b * a.Hq + h) * a.Lq + my_row : nullptr;
+  OutT* orow = (OutT*)a.out + (q_row0 + my_row) * D;
+  float* lse_dst = a.lse ? a.lse + q_row0 + my_row : nullptr;
   finalize_store<D / 32, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
   if (MAXL) store_max_logit(a, row, wk.b, h, my_row, row_valid, half, lane);
 }
@@ -638,8 +677,8 @@ template <bool OUT, bool MAXL>
 hipError_t launch_typed(const FwdArgs& a, int D, bool in_f32, hipStream_t stream) {
   if (!in_f32) {
     const int HG = bf_heads_per_group(a.Hq / a.Hkv);
-    return D == 128 ? launch(fwd_bf16_kernel<128, OUT, MAXL>, kBfThreads, a, stream, HG)
-                    : launch(fwd_bf16_kernel<64, OUT, MAXL>, kBfThreads, a, stream, HG);
+    return D == 128 ? launch(fwd_bf16_kernel<128, OUT, MAXL, false>, kBfThreads, a, stream, HG)
+                    : launch(fwd_bf16_kernel<64, OUT, MAXL, false>, kBfThreads, a, stream, HG);
   }
   return D == 128 ? launch(fwd_f32_kernel<128, OUT, MAXL>, kThreads, a, stream, 1)
                   : launch(fwd_f32_kernel<64, OUT, MAXL>, kThreads, a, stream, 1);
@@ -654,6 +693,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.out = out; a.lse = lse;
   a.max_row = max_row; a.max_head = max_head;
+  a.cu_q = a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.window = window;
   a.c = scale * kLog2e;
   a.scale = scale;
@@ -675,6 +716,27 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
                            : launch_typed<true, false>(a, D, in_f32, stream);
   return maxl ? launch_typed<false, true>(a, D, in_f32, stream)
               : launch_typed<false, false>(a, D, in_f32, stream);
+}
+
+hipError_t launch_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                             const int32_t* cu_k, const float* sinks, void* out, float* lse, int B,
+                             int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int D,
+                             int window, float scale, bool out_f32, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.out = out; a.lse = lse;
+  a.max_row = a.max_head = nullptr;
+  a.cu_q = cu_q; a.cu_k = cu_k; a.total_q = total_q; a.total_k = total_k;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = max_seqlen_q; a.Lk = 0; a.window = window;
+  a.c = scale * kLog2e;
+  a.scale = scale;
+  const int HG = bf_heads_per_group(Hq / Hkv);
+  const int rows = kBfWaves / HG * kRowsPerWave;
+  a.n_qtiles = (max_seqlen_q + rows - 1) / rows;
+  if (D == 128)
+    return out_f32 ? launch(fwd_bf16_kernel<128, true, false, true>, kBfThreads, a, stream, HG)
+                   : launch(fwd_bf16_kernel<128, false, false, true>, kBfThreads, a, stream, HG);
+  return out_f32 ? launch(fwd_bf16_kernel<64, true, false, true>, kBfThreads, a, stream, HG)
+                 : launch(fwd_bf16_kernel<64, false, false, true>, kBfThreads, a, stream, HG);
 }
 
 }  // namespace attn

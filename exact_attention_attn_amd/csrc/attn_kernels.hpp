@@ -14,10 +14,26 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, const float* 
                       int Lk, int D, int window, float scale, bool in_f32, bool out_f32,
                       hipStream_t stream);
 
+// Packed batch of sequences (bf16 inputs): q [Hq,total_q,D], k/v [Hkv,total_k,D],
+// cu_q/cu_k [B+1] device offsets; max_seqlen_q bounds every sequence's rows.
+hipError_t launch_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                             const int32_t* cu_k, const float* sinks, void* out, float* lse, int B,
+                             int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int D,
+                             int window, float scale, bool out_f32, hipStream_t stream);
+
 hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
                          float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
                          int max_splits, int window, float scale, hipStream_t stream);
+
+// Split-KV decode over a paged cache: pages [num_pages,Hkv,1<<page_shift,D],
+// block_table [B,max_pages]; Lk_max = max_pages << page_shift.
+hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int32_t* seqlens_k,
+                               const int32_t* num_splits, float* o_part, float* lse_part, int B,
+                               int Hq, int Hkv, int Lk_max, int num_pages, int page_shift,
+                               int max_pages, int D, int max_splits, int window, float scale,
+                               hipStream_t stream);
 
 // num_splits[b] from seqlens_k by policy (ATTN_SPLITS_*); one work-group.
 hipError_t launch_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int Hq, int Hkv,

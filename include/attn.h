@@ -5,9 +5,11 @@
  *   attn_fwd             fused tiled attention forward (prefill): causal +
  *                        sliding window, GQA, learned per-head sink, LSE
  *                        (attn_fwd_max_logit: the same, plus the largest
- *                        pre-softmax logit per row and per head);
+ *                        pre-softmax logit per row and per head;
+ *                        attn_fwd_varlen: a packed batch of sequences);
  *   attn_decode_splitkv  split-KV decode: per-split partial outputs and LSEs
- *                        (attn_decode_plan: split counts chosen on the device);
+ *                        (attn_decode_plan: split counts chosen on the device;
+ *                        attn_decode_splitkv_paged: over a paged cache);
  *   attn_combine         LSE-weighted merge of the valid splits, sink added once.
  *
  * Conventions shared by every call
@@ -101,6 +103,28 @@ int attn_fwd_max_logit(const void* q, const void* k, const void* v, const float*
                        int out_dtype, void* stream);
 
 /*
+ * attn_fwd_varlen -- attn_fwd over a packed batch of sequences of different
+ * lengths (flash-attention profile: varlen batches described by cu_seqlens,
+ * section 1 capabilities and the call flow's cu_seqlens-to-blocks step).
+ *
+ * q    [Hq,  total_q, D] bf16 -- each head's rows of all sequences, packed
+ * k, v [Hkv, total_k, D] bf16
+ * cu_seqlens_q, cu_seqlens_k [B+1] int32 (device): sequence b owns query
+ *      rows [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]); offsets are
+ *      clamped into [0, total] in the kernel (a decreasing pair is empty).
+ * out  [Hq, total_q, D] out_dtype;  lse [Hq, total_q] float32 or NULL
+ * max_seqlen_q >= every sequence's query count (it sizes the grid; rows of a
+ *      longer sequence past it are not written).
+ * Within a sequence everything is as in attn_fwd (its queries are its last
+ * Lq_b positions); a row that sees no key (Lk_b = 0, or Lq_b > Lk_b) gets
+ * O = 0 and LSE = sink.  in_dtype must be ATTN_BF16.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, const float* sinks, void* out, float* lse, int B,
+                    int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int D, int window,
+                    float scale, int in_dtype, int out_dtype, void* stream);
+
+/*
  * attn_decode_splitkv -- one query per sequence over a KV cache, cut into splits.
  *
  * Split-KV decode (flash-attention profile: split-KV benchmarks; FlashMLA
@@ -126,6 +150,25 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
                         float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
                         int max_splits, int window, float scale, int in_dtype, void* stream);
+
+/*
+ * attn_decode_splitkv_paged -- attn_decode_splitkv over a paged KV cache
+ * (flash-attention profile: paged KV with a block_table for serving decode).
+ *
+ * k_pages, v_pages [num_pages, Hkv, page_size, D] bf16: a pool of pages.
+ * block_table [B, max_pages_per_seq] int32 (device): key j of sequence b is
+ *      row j % page_size of page block_table[b][j / page_size].  Only the
+ *      slots of keys < seqlens_k[b] are read; a page id outside
+ *      [0, num_pages) is clamped into it (wrong values, never a stray access).
+ * page_size: a power of two.  Lk_max of the split rule and of attn_combine
+ * is max_pages_per_seq * page_size.  Everything else is attn_decode_splitkv.
+ */
+int attn_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* seqlens_k,
+                              const int32_t* num_splits, float* o_part, float* lse_part, int B,
+                              int Hq, int Hkv, int num_pages, int page_size, int max_pages_per_seq,
+                              int D, int max_splits, int window, float scale, int in_dtype,
+                              void* stream);
 
 /*
  * attn_decode_plan -- choose num_splits[b] for attn_decode_splitkv on the

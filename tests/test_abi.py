@@ -32,8 +32,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_decode_splitkv", "attn_decode_plan",
-                          "attn_combine", "attn_strerror", "attn_version"}
+    assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_decode_splitkv",
+                          "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine",
+                          "attn_strerror", "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.attn_version().decode().startswith("attn-mi355x")
@@ -151,3 +152,43 @@ def plan(lib, **kw):
 ])
 def test_plan_rejects(lib, kw, code):
     assert plan(lib, **kw) == code
+
+
+def varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, cq=P, ck=P, sinks=P, out=P, lse=P, B=3, Hq=8, Hkv=2, tq=100, tk=120,
+             mq=50, D=128, window=0, scale=0.1, ind=0, outd=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_varlen(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["sinks"], a["out"],
+                               a["lse"], a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"],
+                               a["D"], a["window"], a["scale"], a["ind"], a["outd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(cq=None), 1), (dict(ck=None), 1), (dict(out=None), 1),
+    (dict(B=0), 2), (dict(tq=0), 2), (dict(tk=-1), 2), (dict(mq=0), 2), (dict(mq=101), 2),
+    (dict(Hq=7), 2), (dict(B=70000), 2), (dict(D=96), 3), (dict(ind=1), 3), (dict(outd=5), 3),
+    (dict(scale=0.0), 4), (dict(q=P + 8), 4), (dict(cq=P + 2), 4), (dict(lse=P + 1), 4),
+])
+def test_varlen_rejects(lib, kw, code):
+    assert varlen(lib, **kw) == code
+
+
+def paged(lib, **kw):
+    a = dict(q=P, kp=P, vp=P, bt=P, sl=P, ns=P, op=P, lp=P, B=4, Hq=8, Hkv=2, npg=100, ps=16,
+             mp=10, D=128, ms=64, window=0, scale=0.1, ind=0, stream=None)
+    a.update(kw)
+    return lib.attn_decode_splitkv_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["ns"],
+                                         a["op"], a["lp"], a["B"], a["Hq"], a["Hkv"], a["npg"],
+                                         a["ps"], a["mp"], a["D"], a["ms"], a["window"],
+                                         a["scale"], a["ind"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(bt=None), 1), (dict(kp=None), 1), (dict(lp=None), 1),
+    (dict(B=0), 2), (dict(npg=0), 2), (dict(ps=0), 2), (dict(ps=24), 2), (dict(mp=0), 2),
+    (dict(ms=65), 2), (dict(Hq=6, Hkv=4), 2), (dict(mp=1 << 27, ps=1 << 5), 2),
+    (dict(D=80), 3), (dict(ind=1), 3), (dict(scale=-1.0), 4), (dict(bt=P + 2), 4),
+    (dict(kp=P + 8), 4),
+])
+def test_paged_rejects(lib, kw, code):
+    assert paged(lib, **kw) == code
