@@ -33,6 +33,10 @@ GPU sees, i.e. bf16 or fp32 values upcast):
   the sink exactly once as one more logit (FlashMLA patch stack page, section
   3 "exact small-split combine").
 
+* ``attention_bwd`` -- dQ, dK, dV and dsink of the forward for a given dO,
+  the plain gradient formulas in float64 (the flash-attention profile's
+  two-phase backward; its dsink precision issue #2969).
+
 * ``max_logit_rows`` / ``max_logit`` -- the largest pre-softmax logit
   scale*<q_i,k_j> over the keys each row sees (sink excluded), per row and
   per head (flash-attention contribution-radar profile, task card for issue
@@ -176,6 +180,82 @@ def attention_fwd(q, k, v, sinks, window: int, scale: float, block: int = 256):
                 out[b, h, r0:r0 + len(rows)] = o
                 lse[b, h, r0:r0 + len(rows)] = l
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# backward (gradients of a scalar loss L through O, given dO = dL/dO)
+# ---------------------------------------------------------------------------
+
+def _bwd_block(Q, K, V, dO, sigma, sc, ranges, lo):
+    """Gradients of one block of rows of one (b, h) over keys [lo, lo+K.shape[0]).
+
+    With P_ij = e^{s_ij - LSE_i} (the sink inside LSE), Psink_i = e^{sigma - LSE_i},
+    O = P V and D_i = <dO_i, O_i>:
+        dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+        dQ = scale dS K,  dK = scale dS^T Q,  dsink = -sum_i Psink_i D_i.
+    The sink has no value vector, so it enters dS only through D.
+    """
+    R, N = Q.shape[0], K.shape[0]
+    S = sc * (Q @ K.T)
+    cols = np.arange(lo, lo + N)
+    for r, (a, z) in enumerate(ranges):
+        S[r, (cols < a) | (cols >= z)] = -np.inf
+    row_max = S.max(axis=1) if N else np.full(R, -np.inf)
+    M = np.maximum(row_max, sigma)
+    ok = np.isfinite(M)
+    P = np.zeros((R, N))
+    psink = np.zeros(R)
+    if ok.any():
+        e = np.exp(S[ok] - M[ok, None])
+        es = np.exp(sigma - M[ok]) if np.isfinite(sigma) else np.zeros(int(ok.sum()))
+        den = e.sum(axis=1) + es
+        P[ok] = e / den[:, None]
+        psink[ok] = es / den
+    O = P @ V
+    Dv = (dO * O).sum(axis=1)
+    dP = dO @ V.T
+    dS = P * (dP - Dv[:, None])
+    return sc * (dS @ K), sc * (dS.T @ Q), P.T @ dO, -float((psink * Dv).sum())
+
+
+def attention_bwd(q, k, v, sinks, dout, window: int, scale: float, block: int = 256):
+    """dQ [B,Hq,Lq,D], dK, dV [B,Hkv,Lk,D] and dsink [Hq] of the forward above.
+
+    Plain float64 definition of the gradients (flash-attention profile: the
+    backward takes dO and computes dK/dV and dQ in two phases; the dsink
+    precision issue #2969 is why D_i = <dO_i, O_i> is taken from the float64
+    O here).  Query heads of a GQA group add into their shared KV head; dsink
+    sums over every batch and row.  Rows are taken ``block`` at a time only to
+    bound memory.
+    """
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    sc = effective_scale(scale)
+    dq = np.zeros((B, Hq, Lq, D))
+    dk = np.zeros((B, Hkv, Lk, D))
+    dv = np.zeros((B, Hkv, Lk, D))
+    dsink = np.zeros(Hq)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = kv_head_of(h, Hq, Hkv)
+            sigma = -np.inf if sinks is None else float(np.float64(sinks[h]))
+            for r0 in range(0, Lq, block):
+                rows = range(r0, min(Lq, r0 + block))
+                ranges = [visible_range(query_position(i, Lq, Lk), Lk, window) for i in rows]
+                lo = min(r[0] for r in ranges)
+                hi = max(max(r[1] for r in ranges), lo)
+                Q = np.asarray(q[b, h, r0:r0 + len(rows)], dtype=np.float64)
+                dO = np.asarray(dout[b, h, r0:r0 + len(rows)], dtype=np.float64)
+                K = np.asarray(k[b, kvh, lo:hi], dtype=np.float64)
+                V = np.asarray(v[b, kvh, lo:hi], dtype=np.float64)
+                gq, gk, gv, gs = _bwd_block(Q, K, V, dO, sigma, sc, ranges, lo)
+                dq[b, h, r0:r0 + len(rows)] = gq
+                dk[b, kvh, lo:hi] += gk
+                dv[b, kvh, lo:hi] += gv
+                dsink[h] += gs
+    return dq, dk, dv, dsink
 
 
 # ---------------------------------------------------------------------------

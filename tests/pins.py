@@ -409,3 +409,90 @@ def err_varlen_brute(seed=0, Hq=2, Hkv=1, D=3, window=3):
         worst = max(worst, np.abs(o[:, cu_q[b]:cu_q[b + 1]] - ob[0]).max(),
                     np.abs(l[:, cu_q[b]:cu_q[b + 1]] - lb[0]).max())
     return worst
+
+
+# --- backward ---------------------------------------------------------------------
+
+def loss_fd(q, k, v, sinks, dout, window, scale):
+    """L = <dout, O> from the forward oracle (for finite differences)."""
+    o, _ = oracle.attention_fwd(q, k, v, sinks, window, scale)
+    return float((np.asarray(dout) * o).sum())
+
+
+def err_bwd_finite_diff(seed=0, B=1, Hq=2, Hkv=1, Lq=5, Lk=6, D=3, window=3, eps=1e-6):
+    """Largest |analytic - central difference| over every element of q, k, v, sinks."""
+    q, k, v = rand((B, Hq, Lq, D), seed), rand((B, Hkv, Lk, D), seed + 1), rand((B, Hkv, Lk, D), seed + 2)
+    sinks = rand(Hq, seed + 3)
+    dout = rand((B, Hq, Lq, D), seed + 4)
+    dq, dk, dv, ds = oracle.attention_bwd(q, k, v, sinks, dout, window, 0.6)
+    worst = 0.0
+    for x, g in ((q, dq), (k, dk), (v, dv), (sinks, ds)):
+        flat, gflat = x.reshape(-1), g.reshape(-1)
+        for n in range(flat.size):
+            old = flat[n]
+            flat[n] = old + eps
+            lp = loss_fd(q, k, v, sinks, dout, window, 0.6)
+            flat[n] = old - eps
+            lm = loss_fd(q, k, v, sinks, dout, window, 0.6)
+            flat[n] = old
+            worst = max(worst, abs((lp - lm) / (2 * eps) - gflat[n]))
+    return worst
+
+
+def torch_bwd(q, k, v, sinks, dout, window, scale):
+    """Gradients by torch autograd in float64: logits with the sink as one more
+    column (no value vector), index-built mask, GQA by repeat_interleave."""
+    t = lambda x: torch.tensor(np.asarray(x, np.float64), requires_grad=True)
+    qt, kt, vt, st = t(q), t(k), t(v), t(sinks)
+    B, Hq, Lq, D = qt.shape
+    Hkv, Lk = kt.shape[1], kt.shape[2]
+    G = Hq // Hkv
+    kr, vr = kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1)
+    sc = float(np.float32(scale))
+    s = sc * torch.matmul(qt, kr.transpose(-1, -2))
+    pos = torch.arange(Lq).unsqueeze(1) + (Lk - Lq)
+    key = torch.arange(Lk).unsqueeze(0)
+    keep = key <= pos
+    if window > 0:
+        keep &= key > pos - window
+    s = s.masked_fill(~keep, -math.inf)
+    logits = torch.cat([s, st.view(1, Hq, 1, 1).expand(B, Hq, Lq, 1)], dim=3)
+    p = torch.softmax(logits, dim=3)[..., :Lk]
+    o = torch.matmul(p, vr)
+    (o * torch.tensor(np.asarray(dout, np.float64))).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy(), st.grad.numpy()
+
+
+def err_bwd_torch(seed=0, B=2, Hq=4, Hkv=2, Lq=40, Lk=55, D=8, window=9):
+    q, k, v = rand((B, Hq, Lq, D), seed), rand((B, Hkv, Lk, D), seed + 1), rand((B, Hkv, Lk, D), seed + 2)
+    sinks = rand(Hq, seed + 3, 2.0)
+    dout = rand((B, Hq, Lq, D), seed + 4)
+    got = oracle.attention_bwd(q, k, v, sinks, dout, window, 0.35, block=17)
+    want = torch_bwd(q, k, v, sinks, dout, window, 0.35)
+    return max(np.abs(a - b).max() for a, b in zip(got, want))
+
+
+def err_bwd_gqa(seed=0, Hq=6, Hkv=2, L=20, D=4, window=5):
+    """GQA gradients: dK, dV of a KV head are the sums over its repeated MHA copies."""
+    q, k, v = rand((1, Hq, L, D), seed), rand((1, Hkv, L, D), seed + 1), rand((1, Hkv, L, D), seed + 2)
+    sinks, dout = rand(Hq, seed + 3), rand((1, Hq, L, D), seed + 4)
+    G = Hq // Hkv
+    dq, dk, dv, ds = oracle.attention_bwd(q, k, v, sinks, dout, window, 0.5)
+    dq2, dk2, dv2, ds2 = oracle.attention_bwd(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1),
+                                              sinks, dout, window, 0.5)
+    fold = lambda x: x.reshape(1, Hkv, G, L, D).sum(axis=2)
+    return max(np.abs(dq - dq2).max(), np.abs(dk - fold(dk2)).max(), np.abs(dv - fold(dv2)).max(),
+               np.abs(ds - ds2).max())
+
+
+def err_bwd_shift_invariance(seed=0, Hq=2, L=30, D=4, window=7):
+    """Shifting every logit and the sink by c leaves O unchanged, so with all keys
+    equal to one vector u, dsink = -sum_i <dQ_i, u> / (scale |u|^2)."""
+    u = np.array([0.3, -0.2, 0.5, 0.1])
+    k = np.broadcast_to(u, (1, 1, L, D)).copy()
+    q, v = rand((1, Hq, L, D), seed), rand((1, 1, L, D), seed + 2)
+    sinks, dout = rand(Hq, seed + 3), rand((1, Hq, L, D), seed + 4)
+    sc = float(np.float32(0.5))
+    dq, _, _, ds = oracle.attention_bwd(q, k, v, sinks, dout, window, 0.5)
+    want = -(dq[0] @ u).sum(axis=1) / (sc * float(u @ u))
+    return np.abs(ds - want).max()

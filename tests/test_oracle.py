@@ -456,3 +456,69 @@ def test_paged_varlen_pins_catch_mistakes(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(oa, "attention_fwd", global_positions)
         assert pins.err_varlen_brute(window=3) > 1e-6
+
+
+# --- backward -----------------------------------------------------------------------
+
+@pytest.mark.parametrize("window,Lq,Lk", [(3, 5, 6), (0, 4, 4), (1, 3, 5), (10, 6, 6)])
+def test_bwd_finite_differences(window, Lq, Lk):
+    assert pins.err_bwd_finite_diff(window=window, Lq=Lq, Lk=Lk) < 1e-7
+
+
+def test_bwd_finite_differences_gqa_and_dominant_sink():
+    assert pins.err_bwd_finite_diff(Hq=4, Hkv=2, seed=3) < 1e-7
+
+
+@pytest.mark.parametrize("window", [0, 9])
+def test_bwd_torch_autograd(window):
+    assert pins.err_bwd_torch(window=window) < 1e-10
+
+
+def test_bwd_gqa_is_summed_mha():
+    assert pins.err_bwd_gqa() < 1e-12
+
+
+def test_bwd_shift_invariance():
+    assert pins.err_bwd_shift_invariance() < 1e-10
+
+
+def test_bwd_no_sink_means_zero_dsink():
+    q, k, v = pins.rand((1, 2, 6, 3), 0), pins.rand((1, 1, 6, 3), 1), pins.rand((1, 1, 6, 3), 2)
+    dq, dk, dv, ds = oracle.attention_bwd(q, k, v, None, pins.rand((1, 2, 6, 3), 3), 0, 0.5)
+    assert np.all(ds == 0.0)
+
+
+def _bwd_caught(monkeypatch, name, fake):
+    with monkeypatch.context() as m:
+        m.setattr(oa, name, fake)
+        errs = [pins.err_bwd_torch(window=9), pins.err_bwd_finite_diff(window=3)]
+    return max(errs) > 1e-6
+
+
+def test_bwd_pins_catch_mistakes(monkeypatch):
+    orig = oa._bwd_block
+
+    def no_D(Q, K, V, dO, sigma, sc, ranges, lo):       # dS = P * dP (the D term dropped)
+        S = sc * (Q @ K.T)
+        cols = np.arange(lo, lo + K.shape[0])
+        for r, (a, z) in enumerate(ranges):
+            S[r, (cols < a) | (cols >= z)] = -np.inf
+        M = np.maximum(S.max(axis=1), sigma)
+        e = np.exp(S - M[:, None])
+        den = e.sum(axis=1) + np.exp(sigma - M)
+        P = e / den[:, None]
+        dS = P * (dO @ V.T)
+        _, _, gv, gs = orig(Q, K, V, dO, sigma, sc, ranges, lo)
+        return sc * (dS @ K), sc * (dS.T @ Q), gv, gs
+    assert _bwd_caught(monkeypatch, "_bwd_block", no_D)
+
+    def flipped_dsink(*a):
+        gq, gk, gv, gs = orig(*a)
+        return gq, gk, gv, -gs
+    assert _bwd_caught(monkeypatch, "_bwd_block", flipped_dsink)
+
+    def unscaled_dk(Q, K, V, dO, sigma, sc, ranges, lo):
+        gq, gk, gv, gs = orig(Q, K, V, dO, sigma, sc, ranges, lo)
+        return gq, gk / sc, gv, gs
+    assert _bwd_caught(monkeypatch, "_bwd_block", unscaled_dk)
+    assert _bwd_caught(monkeypatch, "kv_head_of", lambda h, Hq, Hkv: h % Hkv)
