@@ -146,6 +146,44 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
     return rows
 
 
+def measure_backward(A, torch, dev, stream, q, k, v, s, wp, reps=10):
+    """attn_bwd on the step's prefill: dQ, dK, dV and dsink for a seeded dO.
+
+    Algorithmic work is the five products of the backward (S, dP, dV, dK, dQ:
+    10*D flops per unmasked pair, 2.5x the forward); the dQ phase recomputes
+    S and dP, so the kernels execute 14*D per pair.
+    """
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    ds = torch.empty(s.shape, dtype=torch.float32, device=dev)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    with torch.cuda.stream(stream):
+        A.attn_fwd(q, k, v, s, o, lse, window=wp.window, scale=wp.scale, stream=stream)
+        run = lambda: A.attn_bwd(q, k, v, s, o, dout, lse, dq, dk, dv, ds, delta, window=wp.window,
+                                 scale=wp.scale, stream=stream)
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    pairs = wp.flops() // (4 * wp.D)
+    return {"entry": "attn_bwd (dQ, dK, dV, dsink)", "ms": round(t * 1e3, 4),
+            "TFLOP/s": round(10 * wp.D * pairs / t / 1e12, 2),
+            "executed_TFLOP/s": round(14 * wp.D * pairs / t / 1e12, 2),
+            "note": "TFLOP/s counts the 5 backward products (10*D per pair); the dQ phase "
+                    "recomputes S and dP (14*D per pair executed)"}
+
+
 def pairs_window(L: int, W: int) -> int:
     """Unmasked (query, key) pairs of one head: sum_i min(i + 1, W) (W <= 0: causal)."""
     if W <= 0 or W >= L:
@@ -351,6 +389,8 @@ def main():
         A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
         t_dec.mean() + t_cmb.mean(), wp)
 
+    bwd = None if args.step_only else measure_backward(A, torch, dev, stream, q, k, v, s, wp)
+
     t_ml = None
     if not args.step_only:
         # attn_fwd_max_logit (per-row and per-head maxima) on the same prefill,
@@ -437,6 +477,7 @@ def main():
         },
     }
     if not args.step_only:
+        res["backward"] = bwd
         res["split_policy"] = split_policy
         res["serving"] = serving
         res["max_logit"] = {

@@ -13,7 +13,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_decode_splitkv",
+__all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_bwd", "attn_decode_splitkv",
            "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine", "attn_strerror", "AttnError",
            "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
 
@@ -38,6 +38,7 @@ _SIGNATURES = {
     "attn_combine": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "attn_decode_plan": [_vp, _vp] + [_i] * 8 + [_vp],
     "attn_fwd_varlen": [_vp] * 8 + [_i] * 8 + [_f, _i, _i, _vp],
+    "attn_bwd": [_vp] * 12 + [_i] * 7 + [_f, _i, _i, _vp],
     "attn_decode_splitkv_paged": [_vp] * 8 + [_i] * 9 + [_f, _i, _vp],
     "attn_strerror": [_i],
     "attn_version": [],
@@ -233,6 +234,42 @@ def attn_decode_splitkv_paged(q, k_pages, v_pages, block_table, seqlens_k, num_s
         _dev(lse_part, "lse_part", torch.float32), B, Hq, Hkv, num_pages, page_size, max_pages, D,
         max_splits, int(window), float(scale), _dtype_code(q), _stream(stream))
     _check("attn_decode_splitkv_paged", rc)
+
+
+def attn_bwd(q, k, v, sinks, out, dout, lse, dq, dk, dv, dsink=None, delta=None, *,
+             window: int = 0, scale: float | None = None, stream=None) -> None:
+    """dQ, dK, dV (and dsink) of attn_fwd for a given dO.
+
+    q, dout [B,Hq,Lq,D] bf16; k, v [B,Hkv,Lk,D] bf16; out, lse: what attn_fwd
+    returned (out bf16 or fp32 -- fp32 keeps dsink exact); dq, dk, dv fp32;
+    dsink [Hq] fp32 or None; delta [B,Hq,Lq] fp32 workspace (allocated here
+    when None).
+    """
+    import torch
+
+    B, Hq, Lq, D = q.shape
+    _, Hkv, Lk, _ = k.shape
+    for name, t, shape in (("v", v, k.shape), ("out", out, q.shape), ("dout", dout, q.shape),
+                           ("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape),
+                           ("lse", lse, (B, Hq, Lq))):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must be {tuple(shape)}")
+    if sinks is not None and tuple(sinks.shape) != (Hq,):
+        raise ValueError("sinks must be [Hq]")
+    if dsink is not None and tuple(dsink.shape) != (Hq,):
+        raise ValueError("dsink must be [Hq]")
+    if delta is None:
+        delta = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = D ** -0.5
+    rc = load_library().attn_bwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(sinks, "sinks", torch.float32), _dev(out, "out"),
+        _dev(dout, "dout", torch.bfloat16), _dev(lse, "lse", torch.float32),
+        _dev(dq, "dq", torch.float32), _dev(dk, "dk", torch.float32), _dev(dv, "dv", torch.float32),
+        _dev(dsink, "dsink", torch.float32), _dev(delta, "delta", torch.float32),
+        B, Hq, Hkv, Lq, Lk, D, int(window), float(scale), _dtype_code(q), _dtype_code(out),
+        _stream(stream))
+    _check("attn_bwd", rc)
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_part, *,

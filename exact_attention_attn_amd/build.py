@@ -17,12 +17,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_api.cpp"]
 # Per-source code-generation options.  The forward kernel keeps its MFMA
 # accumulators in architectural VGPRs: the softmax rescales them with VALU
 # instructions, and accumulators in AGPRs would be copied back and forth
 # around that (rarely taken) branch on every tile.
-SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the code object.

@@ -80,6 +80,24 @@ int attn_fwd_max_logit(const void* q, const void* k, const void* v, const float*
                                    out_dtype == ATTN_F32, static_cast<hipStream_t>(stream)));
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+             const void* dout, const float* lse, float* dq, float* dk, float* dv, float* dsink,
+             float* delta, int B, int Hq, int Hkv, int Lq, int Lk, int D, int window, float scale,
+             int in_dtype, int out_dtype, void* stream) {
+  int rc = check_fwd(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, out_dtype);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+  if (in_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dsink && !sinks) return ATTN_ERR_VALUE;
+  if ((long long)B * Hq * Lq >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_VALUE;
+  for (const void* p : {(const void*)lse, (const void*)delta, (const void*)sinks, (const void*)dsink})
+    if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return ATTN_ERR_VALUE;
+  return from_hip(attn::launch_bwd(q, k, v, sinks, out, dout, lse, delta, dq, dk, dv, dsink, B, Hq,
+                                   Hkv, Lq, Lk, D, window, scale, out_dtype == ATTN_F32,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                     const int32_t* cu_seqlens_k, const float* sinks, void* out, float* lse, int B,
                     int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int D, int window,

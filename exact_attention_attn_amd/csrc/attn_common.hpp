@@ -60,6 +60,12 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// v_mfma_f32_16x16x32_bf16  A[16x32]: lane l holds row l%16, k = (l/16)*8 + e (e < 8)
+//                           B[32x16]: lane l holds col l%16, k = (l/16)*8 + e
+//                           C[16x16]: lane l, reg r -> row (l/16)*4 + r, col l%16
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x16 mfma_32x32x2(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }

@@ -45,4 +45,12 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, const int3
                           int B, int Hq, int D, int Lk_max, int max_splits, int window,
                           bool out_f32, hipStream_t stream);
 
+// Backward: delta [B,Hq,Lq] workspace (D_i = <dO_i, O_i>), then dsink (when
+// both dsink and sinks are given), dK/dV and dQ; every output fp32.
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* sinks,
+                      const void* out, const void* dout, const float* lse, float* delta,
+                      float* dq, float* dk, float* dv, float* dsink, int B, int Hq, int Hkv,
+                      int Lq, int Lk, int D, int window, float scale, bool o_f32,
+                      hipStream_t stream);
+
 }  // namespace attn

@@ -6,7 +6,8 @@
  *                        sliding window, GQA, learned per-head sink, LSE
  *                        (attn_fwd_max_logit: the same, plus the largest
  *                        pre-softmax logit per row and per head;
- *                        attn_fwd_varlen: a packed batch of sequences);
+ *                        attn_fwd_varlen: a packed batch of sequences;
+ *                        attn_bwd: dQ, dK, dV and dsink for a given dO);
  *   attn_decode_splitkv  split-KV decode: per-split partial outputs and LSEs
  *                        (attn_decode_plan: split counts chosen on the device;
  *                        attn_decode_splitkv_paged: over a paged cache);
@@ -123,6 +124,33 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
                     const int32_t* cu_seqlens_k, const float* sinks, void* out, float* lse, int B,
                     int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int D, int window,
                     float scale, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * attn_bwd -- gradients of a loss through attn_fwd, given dO = dL/dO.
+ *
+ * With P_ij = exp(s_ij - LSE_i), Psink_i = exp(sink - LSE_i) (LSE of attn_fwd,
+ * the sink included) and D_i = <dO_i, O_i>:  dV = P^T dO,  dS = P (dO V^T - D),
+ * dQ = scale dS K,  dK = scale dS^T Q,  dsink_h = -sum_{b,i} Psink_i D_i.
+ * The flash-attention profile's backward: a dK/dV phase and a dQ phase.  Its
+ * issue #2969 is that dsink loses precision when D comes from a bf16-rounded
+ * O; here dsink uses D_i = sum_j P_ij (dO_i . v_j) summed in fp32 inside the
+ * dQ phase, which does not depend on O at all.  O (bf16 or fp32) only feeds
+ * the D of dS.
+ *
+ * q, dout [B,Hq,Lq,D] bf16; k, v [B,Hkv,Lk,D] bf16 (in_dtype must be ATTN_BF16)
+ * out  [B,Hq,Lq,D] out_dtype: the O that attn_fwd returned for these inputs
+ * lse  [B,Hq,Lq] float32: the LSE that attn_fwd returned
+ * sinks [Hq] or NULL; mask, window, GQA and scale as in attn_fwd
+ * dq [B,Hq,Lq,D], dk, dv [B,Hkv,Lk,D] float32 (fully written; GQA heads add
+ *      into their KV head); dsink [Hq] float32 or NULL (requires sinks)
+ * delta [B,Hq,Lq] float32: caller-owned workspace (D_i), overwritten; on
+ *      return it holds sum_j P_ij dP_ij.
+ * Deterministic: no atomics; every sum has a fixed order.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+             const void* dout, const float* lse, float* dq, float* dk, float* dv, float* dsink,
+             float* delta, int B, int Hq, int Hkv, int Lq, int Lk, int D, int window, float scale,
+             int in_dtype, int out_dtype, void* stream);
 
 /*
  * attn_decode_splitkv -- one query per sequence over a KV cache, cut into splits.

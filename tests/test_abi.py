@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_decode_splitkv",
+    assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_bwd", "attn_decode_splitkv",
                           "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine",
                           "attn_strerror", "attn_version"}
     for n in names:
@@ -192,3 +192,23 @@ def paged(lib, **kw):
 ])
 def test_paged_rejects(lib, kw, code):
     assert paged(lib, **kw) == code
+
+
+def bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, sinks=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, dsink=P, delta=P, B=1,
+             Hq=8, Hkv=2, Lq=10, Lk=10, D=128, window=0, scale=0.1, ind=0, outd=1, stream=None)
+    a.update(kw)
+    return lib.attn_bwd(a["q"], a["k"], a["v"], a["sinks"], a["out"], a["dout"], a["lse"], a["dq"],
+                        a["dk"], a["dv"], a["dsink"], a["delta"], a["B"], a["Hq"], a["Hkv"],
+                        a["Lq"], a["Lk"], a["D"], a["window"], a["scale"], a["ind"], a["outd"],
+                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=None), 1), (dict(delta=None), 1), (dict(Hq=7), 2), (dict(Lq=11), 2), (dict(B=0), 2),
+    (dict(D=96), 3), (dict(ind=1), 3), (dict(outd=3), 3), (dict(scale=0.0), 4),
+    (dict(sinks=None), 4), (dict(dq=P + 4), 4), (dict(delta=P + 2), 4), (dict(dout=P + 8), 4),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
