@@ -145,6 +145,9 @@ __device__ __forceinline__ u32x4 lds_read16(const lds_char* base, int off) {
 __device__ __forceinline__ void lds_write16(lds_char* base, int off, u32x4 v) {
   *(__attribute__((address_space(3))) u32x4*)(base + off) = v;
 }
+__device__ __forceinline__ void lds_write8(lds_char* base, int off, u32x2 v) {
+  *(__attribute__((address_space(3))) u32x2*)(base + off) = v;
+}
 __device__ __forceinline__ i16x4 lds_read_tr16(const lds_char* base, int off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(base + off));

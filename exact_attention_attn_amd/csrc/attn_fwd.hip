@@ -108,6 +108,71 @@ __device__ __forceinline__ void finalize_store(const f32x16 (&o)[NDB], Row row, 
   if (lse_dst && half == 0) *lse_dst = lse;
 }
 
+// Finalise with the sink and store the wave's block of 32 consecutive output
+// rows through LDS.  The MFMA layout gives a lane one row and runs of 4
+// consecutive d, so direct stores would touch 32 rows per instruction; here
+// each lane writes its runs into a row-major staging block (16 B chunks
+// XOR-swizzled by row against bank conflicts) and the wave reads it back as
+// whole rows, CH lanes per row, so that every global store instruction writes
+// 64/CH complete rows.  A wave reads back only what it wrote, and LDS
+// operations of one wave complete in order, so no barrier is needed.
+template <int D, typename OutT>
+__device__ __forceinline__ void finalize_store_rows(const f32x16 (&o)[D / 32], Row row,
+                                                    float sink_l2, lds_char* stage, OutT* oblock,
+                                                    int nrows, float* lse_dst, int col, int half,
+                                                    int lane) {
+  constexpr int ROWB = D * (int)sizeof(OutT);  // bytes of one output row
+  constexpr int CH = ROWB / 16;                // 16 B chunks per row (8 .. 32)
+  constexpr int RPI = 64 / CH;                 // rows per store instruction
+  float l_tot = pair_sum(row.l);
+  float m_fin = fmaxf(row.m, sink_l2);
+  float scale_o = 0.0f, lse = kNegInf;
+  if (m_fin != kNegInf) {
+    float r = exp2_fast(row.m - m_fin);  // row.m = -inf (no key) -> 0
+    float den = l_tot * r + exp2_fast(sink_l2 - m_fin);
+    scale_o = r / den;
+    lse = (m_fin + log2_fast(den)) * kLn2;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int byte = (db * 32 + j * 8 + half * 4) * (int)sizeof(OutT);
+      const int off = col * ROWB + ((((byte >> 4) ^ (col & (CH - 1))) << 4) | (byte & 15));
+      const float x0 = o[db][j * 4 + 0] * scale_o, x1 = o[db][j * 4 + 1] * scale_o;
+      const float x2 = o[db][j * 4 + 2] * scale_o, x3 = o[db][j * 4 + 3] * scale_o;
+      if constexpr (sizeof(OutT) == 4)
+        lds_write16(stage, off, __builtin_bit_cast(u32x4, ((f32x4){x0, x1, x2, x3})));
+      else
+        lds_write8(stage, off, (u32x2){pack2_bf16(x0, x1), pack2_bf16(x2, x3)});
+    }
+  }
+  const int rr = lane / CH, cc = lane % CH;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / RPI; ++i) {
+    const int r = i * RPI + rr;
+    const u32x4 v = lds_read16(stage, r * ROWB + ((cc ^ (r & (CH - 1))) << 4));
+    if (r < nrows) *(u32x4*)((char*)oblock + (size_t)r * ROWB + cc * 16) = v;
+  }
+  if (lse_dst && half == 0 && col < nrows) *lse_dst = lse;
+}
+
+// Copy a block of 32 consecutive bf16 rows (nrows of them present; the rest
+// arrive as zeros) into LDS in the BfTile layout, 1 KB per copy instruction.
+template <int D>
+__device__ __forceinline__ void copy_rows_to_lds(const uint16_t* src, int nrows, lds_char* dst,
+                                                 int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using L = BfLayout<D>;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)src, 0, max(nrows, 0) * L::kRow, kRawBufferWord3);
+#pragma unroll
+  for (int pc = 0; pc < kRowsPerWave * L::kRow / 1024; ++pc)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + pc * 1024, 16, dma_src_off<D>(pc, lane), 0,
+                                             0, 0);
+#endif
+}
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -327,21 +392,34 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int key_hi = wg_span.p_last + 1;
   const int t_begin = key_lo / kBc, t_end = (key_hi + kBc - 1) / kBc;
 
+  // A wave's 32-row Q and O blocks (32 x D bf16, half of one K/V array) are
+  // staged in LDS: waves 0 and 1 use a K array, waves 2 and 3 the V array.
+  using T = BfTile<D>;
+  const int blk = (wave & 1) * (L::kBytes / 2);
+  const int n_rows = wave_active ? min(kRowsPerWave, Lq - w0) : 0;
+  const int my_row = w0 + col;
+  const bool row_valid = my_row < Lq;
+
+  // Q^T operand: lane holds query row w0+col, d = ks*16 + half*8 .. +8.  The
+  // block comes in through stage 1, idle until the first ring step refills it.
+  bf16x8 qf[D / 16];
+  lds_char* qst = (wave < 2 ? K1 : V1) + blk;
+  copy_rows_to_lds<D>(qh + (size_t)w0 * D, n_rows, qst, lane);
+
   // Two-stage ring: tile t lives in stage (t - t_begin) % 2.
   TileCopy<D> cp;
   cp.init(wave, lane);
   if (t_begin < t_end) cp.issue(kh, vh, t_begin, Lk, K0, V0);  // no tile: no key visible
 
-  // Q^T operand: lane holds query row w0+col, d = ks*16 + half*8 .. +8.
-  const int my_row = w0 + col;
-  const bool row_valid = my_row < Lq;
-  bf16x8 qf[D / 16];
+  // The Q copy was issued before the tile's, so it is done once only the
+  // tile's copies are outstanding.
+  if (t_begin < t_end)
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(2 * L::kPerWave));
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 v = {0, 0, 0, 0};
-    if (row_valid) v = *(const u32x4*)(qh + (size_t)my_row * D + ks * 16 + half * 8);
-    qf[ks] = as_bf16x8(v);
-  }
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = as_bf16x8(lds_read16(qst, T::off(col, (ks * 2 + half) * 16)));
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
@@ -357,7 +435,6 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Per-lane operand read addresses within a stage.  K: row key_perm(col),
   // chunk ks*2 + half.  V (transposed reads): keys half*8 + (lane%16)/4 + 4e,
   // d = db*32 + ((lane/16)%2)*16 + (lane%4)*4.
-  using T = BfTile<D>;
   int ka[D / 16], va[2][D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) ka[ks] = T::off(key_perm(col), (ks * 2 + half) * 16);
@@ -384,10 +461,22 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     step(t + 1, K1, V1, K0, V0);
   }
 
+  // O staging: with bf16 output a wave's block fits the stage that held tile
+  // t_end-2 (every wave passed the last step's barrier after computing it, and
+  // no copy refills it); an f32 block needs a whole K/V array per wave, after
+  // a barrier.
+  lds_char* ost;
+  if constexpr (OUT_F32) {
+    __syncthreads();
+    ost = wave == 0 ? K0 : wave == 1 ? K1 : wave == 2 ? V0 : V1;
+  } else {
+    const bool free0 = ((t_end - t_begin) & 1) == 0;
+    ost = (wave < 2 ? (free0 ? K0 : K1) : (free0 ? V0 : V1)) + blk;
+  }
   const float sink_l2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-  OutT* orow = (OutT*)a.out + (q_row0 + my_row) * D;
+  OutT* oblock = (OutT*)a.out + (q_row0 + w0) * D;
   float* lse_dst = a.lse ? a.lse + q_row0 + my_row : nullptr;
-  finalize_store<D / 32, OutT>(o, row, sink_l2, orow, lse_dst, row_valid, half);
+  finalize_store_rows<D, OutT>(o, row, sink_l2, ost, oblock, n_rows, lse_dst, col, half, lane);
   if (MAXL) store_max_logit(a, row, wk.b, h, my_row, row_valid, half, lane);
 }
 
