@@ -24,6 +24,8 @@
 #include "attn_kernels.hpp"
 #include "attn_tiles.hpp"
 
+#include <type_traits>
+
 namespace attn {
 
 namespace {
@@ -48,50 +50,96 @@ struct BwdArgs {
 
 // ---------------------------------------------------------------------------
 // D_i = <dO_i, O_i>: 16 lanes per row, D/16 elements each, fixed reduction.
+// A 16-lane group takes kDeltaRows rows per pass and issues all their loads
+// (non-temporal: every byte is read once) before the first product.
 // ---------------------------------------------------------------------------
+constexpr int kDeltaRows = 4;
+
 template <int D, bool O_F32>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  constexpr int E = D / 16;
+  constexpr int E = D / 16;  // elements per lane: 8 (D = 128) or 4 (D = 64)
+  constexpr int R = kDeltaRows;
+  using OT = typename std::conditional<O_F32, float, uint16_t>::type;
+  using GV = typename std::conditional<E == 8, u32x4, u32x2>::type;  // E bf16
+  constexpr int ON = E * (int)sizeof(OT) / 16 > 0 ? E * (int)sizeof(OT) / 16 : 1;
+  using OV = typename std::conditional<E * sizeof(OT) >= 16, u32x4, u32x2>::type;
   const long long rows = (long long)a.B * a.Hq * a.Lq;
   const int sub = threadIdx.x & 15;
-  for (long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / 16; row < rows;
-       row += (long long)gridDim.x * 16) {
-    const uint16_t* g = a.dout + row * D + sub * E;
-    float acc = 0.0f;
+  const long long groups = (long long)gridDim.x * 16;
+  for (long long row0 = ((long long)blockIdx.x * 16 + (threadIdx.x >> 4)) * R; row0 < rows;
+       row0 += groups * R) {
+    GV g[R];
+    OV o[R][ON];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float go = __builtin_bit_cast(float, (uint32_t)g[e] << 16);
-      float ov;
-      if constexpr (O_F32)
-        ov = ((const float*)a.o)[row * D + sub * E + e];
-      else
-        ov = __builtin_bit_cast(float, (uint32_t)((const uint16_t*)a.o)[row * D + sub * E + e] << 16);
-      acc = __builtin_fmaf(go, ov, acc);
+    for (int r = 0; r < R; ++r) {
+      const long long row = min(row0 + r, rows - 1);  // in bounds; the extra rows are not stored
+      g[r] = __builtin_nontemporal_load((const GV*)(a.dout + row * D + sub * E));
+#pragma unroll
+      for (int j = 0; j < ON; ++j)
+        o[r][j] = __builtin_nontemporal_load((const OV*)((const OT*)a.o + row * D + sub * E) + j);
     }
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (sub == 0) a.delta[row] = acc;
+    for (int r = 0; r < R; ++r) {
+      const uint16_t* gs = (const uint16_t*)&g[r];
+      const OT* os = (const OT*)&o[r][0];
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float go = __builtin_bit_cast(float, (uint32_t)gs[e] << 16);
+        float ov;
+        if constexpr (O_F32)
+          ov = os[e];
+        else
+          ov = __builtin_bit_cast(float, (uint32_t)os[e] << 16);
+        acc = __builtin_fmaf(go, ov, acc);
+      }
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+      if (sub == 0 && row0 + r < rows) a.delta[row0 + r] = acc;
+    }
   }
 }
 
-// dsink[h] = -sum over (b, i) of exp(sink_h - LSE) * D, one work-group per
-// head, each thread a strided partial sum, then a fixed tree.
-__global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdArgs a) {
-  __shared__ float part[4];
+// dsink[h] = -sum over (b, i) of exp(sink_h - LSE) * D, one work-group of
+// 1024 threads per head: each thread sums a fixed strided subset (kSinkUnroll
+// loads in flight), then a fixed tree.
+constexpr int kSinkThreads = 1024;
+constexpr int kSinkUnroll = 4;
+
+__global__ __launch_bounds__(kSinkThreads) void bwd_dsink_kernel(BwdArgs a) {
+  __shared__ float part[kSinkThreads / 64];
   const int h = blockIdx.x;
   const float sink = a.sinks[h];
   float acc = 0.0f;
   const int n = a.B * a.Lq;
-  for (int idx = threadIdx.x; idx < n; idx += 256) {
-    const int b = idx / a.Lq, i = idx % a.Lq;
-    const size_t r = (size_t)(b * a.Hq + h) * a.Lq + i;
-    const float l = a.lse[r];  // >= sink: the LSE holds the sink term
-    acc -= exp2_fast((sink - l) * kLog2e) * a.delta[r];
+  for (int base = 0; base < n; base += kSinkThreads * kSinkUnroll) {
+    float l[kSinkUnroll], d[kSinkUnroll];
+#pragma unroll
+    for (int u = 0; u < kSinkUnroll; ++u) {
+      const int idx = base + u * kSinkThreads + (int)threadIdx.x;
+      l[u] = 0.0f;  // unused: a missing row's term is skipped below
+      d[u] = 0.0f;
+      if (idx < n) {
+        const int b = idx / a.Lq, i = idx % a.Lq;
+        const size_t r = (size_t)(b * a.Hq + h) * a.Lq + i;
+        l[u] = a.lse[r];  // >= sink: the LSE holds the sink term
+        d[u] = a.delta[r];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSinkUnroll; ++u)
+      if (base + u * kSinkThreads + (int)threadIdx.x < n)
+        acc -= exp2_fast((sink - l[u]) * kLog2e) * d[u];
   }
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) a.dsink[h] = (part[0] + part[1]) + (part[2] + part[3]);
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSinkThreads / 64; ++w) t += part[w];
+    a.dsink[h] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -193,16 +241,19 @@ __global__ __launch_bounds__(kBfThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int my_row = w0 + col;
   const bool row_valid = my_row < a.Lq;
+  const int n_rows = wave_active ? min(kRowsPerWave, a.Lq - w0) : 0;
+  // Q^T and dO^T operands (row w0+col, d = ks*16 + half*8 ..): both 32-row
+  // blocks are loaded with whole-row instructions at once and turned into the
+  // operand layout through the wave's half of K1 / V1, idle until the first
+  // ring step refills it.
   bf16x8 qf[D / 16], df[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (row_valid) {
-      x = *(const u32x4*)(a.q + (q_row0 + my_row) * D + ks * 16 + half * 8);
-      y = *(const u32x4*)(a.dout + (q_row0 + my_row) * D + ks * 16 + half * 8);
-    }
-    qf[ks] = as_bf16x8(x);
-    df[ks] = as_bf16x8(y);
+  {
+    RowBlockRegs<D> qb, gb;
+    qb.load(a.q + (q_row0 + w0) * D, n_rows, lane);
+    gb.load(a.dout + (q_row0 + w0) * D, n_rows, lane);
+    lds_char* region = (wave < 2 ? K1 : V1) + (wave & 1) * (BfLayout<D>::kBytes / 2);
+    qb.to_operand(region, col, half, lane, qf);
+    gb.to_operand(region, col, half, lane, df);  // LDS in order: qf was read first
   }
   // An invalid row gets lse2 = +inf: its P is 0 and it adds nothing.
   const float lse2 = row_valid ? a.lse[q_row0 + my_row] * kLog2e : __builtin_huge_valf();
@@ -247,17 +298,12 @@ __global__ __launch_bounds__(kBfThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // It replaces the workspace value (the dK/dV kernel, earlier on the stream,
   // is done with it) for dsink.
   const float d_exact = pair_sum(dsum);
-  if (!row_valid) return;
-  if (half == 0) a.delta[q_row0 + my_row] = d_exact;
-  float* dst = a.dq + (q_row0 + my_row) * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + j * 8 + half * 4;
-      *(f32x4*)(dst + d) = (f32x4){o[db][j * 4] * a.scale, o[db][j * 4 + 1] * a.scale,
-                                   o[db][j * 4 + 2] * a.scale, o[db][j * 4 + 3] * a.scale};
-    }
+  if (row_valid && half == 0) a.delta[q_row0 + my_row] = d_exact;
+  // dQ (fp32, 16 KB per wave) through a whole K/V array per wave, once every
+  // wave is done with the ring (the last step copies nothing).
+  __syncthreads();
+  lds_char* st = wave == 0 ? K0 : wave == 1 ? K1 : wave == 2 ? V0 : V1;
+  store_rows_staged<D, float>(o, a.scale, st, a.dq + (q_row0 + w0) * D, n_rows, col, half, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -527,7 +573,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* 
   a.n_qtiles = (Lq + rows - 1) / rows;
 
   const long long nrows = (long long)B * Hq * Lq;
-  const int pre_grid = (int)min((nrows + 15) / 16, 65536LL);
+  const int pre_grid = (int)min((nrows + 16 * kDeltaRows - 1) / (16 * kDeltaRows), 65536LL);
   if (D == 128) {
     if (o_f32) hipLaunchKernelGGL((bwd_delta_kernel<128, true>), dim3(pre_grid), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((bwd_delta_kernel<128, false>), dim3(pre_grid), dim3(256), 0, stream, a);
@@ -548,7 +594,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* 
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // dsink from the D_i that the dQ kernel rewrote
-  if (dsink && sinks) hipLaunchKernelGGL(bwd_dsink_kernel, dim3(Hq), dim3(256), 0, stream, a);
+  if (dsink && sinks)
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(Hq), dim3(kSinkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -109,21 +109,12 @@ __device__ __forceinline__ void finalize_store(const f32x16 (&o)[NDB], Row row, 
 }
 
 // Finalise with the sink and store the wave's block of 32 consecutive output
-// rows through LDS.  The MFMA layout gives a lane one row and runs of 4
-// consecutive d, so direct stores would touch 32 rows per instruction; here
-// each lane writes its runs into a row-major staging block (16 B chunks
-// XOR-swizzled by row against bank conflicts) and the wave reads it back as
-// whole rows, CH lanes per row, so that every global store instruction writes
-// 64/CH complete rows.  A wave reads back only what it wrote, and LDS
-// operations of one wave complete in order, so no barrier is needed.
+// rows (staged through LDS, see store_rows_staged) and the LSE.
 template <int D, typename OutT>
 __device__ __forceinline__ void finalize_store_rows(const f32x16 (&o)[D / 32], Row row,
                                                     float sink_l2, lds_char* stage, OutT* oblock,
                                                     int nrows, float* lse_dst, int col, int half,
                                                     int lane) {
-  constexpr int ROWB = D * (int)sizeof(OutT);  // bytes of one output row
-  constexpr int CH = ROWB / 16;                // 16 B chunks per row (8 .. 32)
-  constexpr int RPI = 64 / CH;                 // rows per store instruction
   float l_tot = pair_sum(row.l);
   float m_fin = fmaxf(row.m, sink_l2);
   float scale_o = 0.0f, lse = kNegInf;
@@ -133,44 +124,8 @@ __device__ __forceinline__ void finalize_store_rows(const f32x16 (&o)[D / 32], R
     scale_o = r / den;
     lse = (m_fin + log2_fast(den)) * kLn2;
   }
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int byte = (db * 32 + j * 8 + half * 4) * (int)sizeof(OutT);
-      const int off = col * ROWB + ((((byte >> 4) ^ (col & (CH - 1))) << 4) | (byte & 15));
-      const float x0 = o[db][j * 4 + 0] * scale_o, x1 = o[db][j * 4 + 1] * scale_o;
-      const float x2 = o[db][j * 4 + 2] * scale_o, x3 = o[db][j * 4 + 3] * scale_o;
-      if constexpr (sizeof(OutT) == 4)
-        lds_write16(stage, off, __builtin_bit_cast(u32x4, ((f32x4){x0, x1, x2, x3})));
-      else
-        lds_write8(stage, off, (u32x2){pack2_bf16(x0, x1), pack2_bf16(x2, x3)});
-    }
-  }
-  const int rr = lane / CH, cc = lane % CH;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave / RPI; ++i) {
-    const int r = i * RPI + rr;
-    const u32x4 v = lds_read16(stage, r * ROWB + ((cc ^ (r & (CH - 1))) << 4));
-    if (r < nrows) *(u32x4*)((char*)oblock + (size_t)r * ROWB + cc * 16) = v;
-  }
+  store_rows_staged<D, OutT>(o, scale_o, stage, oblock, nrows, col, half, lane);
   if (lse_dst && half == 0 && col < nrows) *lse_dst = lse;
-}
-
-// Copy a block of 32 consecutive bf16 rows (nrows of them present; the rest
-// arrive as zeros) into LDS in the BfTile layout, 1 KB per copy instruction.
-template <int D>
-__device__ __forceinline__ void copy_rows_to_lds(const uint16_t* src, int nrows, lds_char* dst,
-                                                 int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  using L = BfLayout<D>;
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)src, 0, max(nrows, 0) * L::kRow, kRawBufferWord3);
-#pragma unroll
-  for (int pc = 0; pc < kRowsPerWave * L::kRow / 1024; ++pc)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + pc * 1024, 16, dma_src_off<D>(pc, lane), 0,
-                                             0, 0);
-#endif
 }
 
 struct FwdArgs {

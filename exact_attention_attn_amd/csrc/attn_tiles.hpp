@@ -166,5 +166,97 @@ __host__ __device__ __forceinline__ int bf_heads_per_group(int G) {
   return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
+// ---------------------------------------------------------------------------
+// Row blocks of one wave: 32 consecutive rows of D elements, contiguous in
+// HBM.  The MFMA layouts give a lane one row and runs of 4 or 8 consecutive d,
+// so reading or writing such a block straight from the operand/accumulator
+// registers touches 32 rows per instruction; these helpers go through an LDS
+// block of the wave's own so that every global instruction covers whole rows.
+// A wave reads back only what it wrote itself and LDS operations of one wave
+// complete in order, so they need no barrier.
+// ---------------------------------------------------------------------------
+
+// Store o (MFMA 32x32 accumulators of O^T: lane col = row, d = db*32 + j*8 +
+// half*4 + e in o[db][4j + e]) times mul as rows 0..nrows-1 of oblock (bf16 or
+// fp32).  The LDS block holds rows of D*sizeof(OutT) bytes with 16 B chunks
+// XOR-swizzled by row against bank conflicts; it is read back CH lanes per row.
+template <int D, typename OutT>
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&o)[D / 32], float mul,
+                                                  lds_char* stage, OutT* oblock, int nrows,
+                                                  int col, int half, int lane) {
+  constexpr int ROWB = D * (int)sizeof(OutT);  // bytes of one output row
+  constexpr int CH = ROWB / 16;                // 16 B chunks per row (8 .. 32)
+  constexpr int RPI = 64 / CH;                 // rows per store instruction
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int byte = (db * 32 + j * 8 + half * 4) * (int)sizeof(OutT);
+      const int off = col * ROWB + ((((byte >> 4) ^ (col & (CH - 1))) << 4) | (byte & 15));
+      const float x0 = o[db][j * 4 + 0] * mul, x1 = o[db][j * 4 + 1] * mul;
+      const float x2 = o[db][j * 4 + 2] * mul, x3 = o[db][j * 4 + 3] * mul;
+      if constexpr (sizeof(OutT) == 4)
+        lds_write16(stage, off, __builtin_bit_cast(u32x4, ((f32x4){x0, x1, x2, x3})));
+      else
+        lds_write8(stage, off, (u32x2){pack2_bf16(x0, x1), pack2_bf16(x2, x3)});
+    }
+  }
+  const int rr = lane / CH, cc = lane % CH;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / RPI; ++i) {
+    const int r = i * RPI + rr;
+    const u32x4 v = lds_read16(stage, r * ROWB + ((cc ^ (r & (CH - 1))) << 4));
+    if (r < nrows) *(u32x4*)((char*)oblock + (size_t)r * ROWB + cc * 16) = v;
+  }
+}
+
+// Copy a block of 32 consecutive bf16 rows (nrows of them present; the rest
+// arrive as zeros) into LDS in the BfTile layout, 1 KB per copy instruction.
+template <int D>
+__device__ __forceinline__ void copy_rows_to_lds(const uint16_t* src, int nrows, lds_char* dst,
+                                                 int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using L = BfLayout<D>;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)src, 0, max(nrows, 0) * L::kRow, kRawBufferWord3);
+#pragma unroll
+  for (int pc = 0; pc < kRowsPerWave * L::kRow / 1024; ++pc)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + pc * 1024, 16, dma_src_off<D>(pc, lane), 0,
+                                             0, 0);
+#endif
+}
+
+// Load a block of 32 consecutive bf16 rows into registers, 1 KB of
+// consecutive bytes per load instruction (rows past nrows read as zeros).
+template <int D>
+struct RowBlockRegs {
+  static constexpr int kN = kRowsPerWave * D * 2 / 1024;  // loads per lane
+  u32x4 v[kN];
+  __device__ __forceinline__ void load(const uint16_t* src, int nrows, int lane) {
+    constexpr int CHK = D / 8;  // 16 B chunks per row
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int q = i * 64 + lane;  // chunk index within the block
+      v[i] = (u32x4){0, 0, 0, 0};
+      if (q / CHK < nrows) v[i] = *(const u32x4*)(src + q * 8);
+    }
+  }
+  // Write the block to region (BfTile layout) and read the MFMA operand of
+  // row col back: f[ks] = d ks*16 + half*8 .. +8.
+  __device__ __forceinline__ void to_operand(lds_char* region, int col, int half, int lane,
+                                             bf16x8 (&f)[D / 16]) const {
+    using T = BfTile<D>;
+    constexpr int CHK = D / 8;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int q = i * 64 + lane;
+      lds_write16(region, T::off(q / CHK, (q % CHK) * 16), v[i]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      f[ks] = as_bf16x8(lds_read16(region, T::off(col, (ks * 2 + half) * 16)));
+  }
+};
+
 }  // namespace
 }  // namespace attn
