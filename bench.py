@@ -82,6 +82,29 @@ def decode_bytes(seqlens, Hq, Hkv, D, window) -> int:
     return kv + B * Hq * D * 2 + B * Hq * D * 2 + B * Hq * 4 + Hq * 4
 
 
+def warm_then_time(torch, stream, fn, reps, warm_s=0.04):
+    """Seconds per call of fn on stream, averaged over reps calls, after running
+    it until at least warm_s seconds of GPU time have passed (after an idle
+    spell the first ~20 ms of work run up to a quarter slower)."""
+    with torch.cuda.stream(stream):
+        spent = 0.0
+        while spent < warm_s:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            spent += e0.elapsed_time(e1) * 1e-3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
 def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd,
                            seqlens, reps=20):
     """GB/s of decode + combine under several split-count policies.
@@ -113,15 +136,7 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
                            stream=stream)
         with torch.cuda.stream(stream):
             plan()
-            for _ in range(5):
-                once()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                once()
-            e1.record(stream)
-            torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = warm_then_time(torch, stream, once, reps) * 1e3
         return {"policy": f"{policy}({param})" if policy != "auto" else "auto",
                 "us": round(ms * 1e3, 1), "GB/s": round(nbytes / ms / 1e6, 1),
                 "total_splits": int(ns.sum().item())}
@@ -165,17 +180,9 @@ def measure_backward(A, torch, dev, stream, q, k, v, s, wp, reps=10):
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     with torch.cuda.stream(stream):
         A.attn_fwd(q, k, v, s, o, lse, window=wp.window, scale=wp.scale, stream=stream)
-        run = lambda: A.attn_bwd(q, k, v, s, o, dout, lse, dq, dk, dv, ds, delta, window=wp.window,
-                                 scale=wp.scale, stream=stream)
-        for _ in range(3):
-            run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / reps * 1e-3
+    run = lambda: A.attn_bwd(q, k, v, s, o, dout, lse, dq, dk, dv, ds, delta, window=wp.window,
+                             scale=wp.scale, stream=stream)
+    t = warm_then_time(torch, stream, run, reps)
     pairs = wp.flops() // (4 * wp.D)
     return {"entry": "attn_bwd (dQ, dK, dV, dsink)", "ms": round(t * 1e3, 4),
             "TFLOP/s": round(10 * wp.D * pairs / t / 1e12, 2),
@@ -196,16 +203,7 @@ def measure_serving(A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dls
     """Paged decode (pages shuffled) against the dense decode on the same cache,
     and the varlen forward on a packed batch, each timed with events on stream."""
     def timeit(fn):
-        with torch.cuda.stream(stream):
-            for _ in range(5):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e-3
+        return warm_then_time(torch, stream, fn, reps)
 
     res = {"paged_decode": [], "varlen_prefill": None}
     nbytes = decode_bytes(seqlens, wd.Hq, wd.Hkv, wd.D, wd.window)
