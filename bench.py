@@ -407,6 +407,23 @@ def main():
             torch.cuda.synchronize()
         t_ml = np.array([e0.elapsed_time(e1) for e0, e1 in ml_ev[n_ml // 2:]]) * 1e-3
 
+    # Host time per ABI call (argument checks, marshalling and the launch), the
+    # calls left to run asynchronously; the GPU work of 50 calls fits the queue.
+    def host_us(fn, n=50):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        h1 = time.perf_counter()
+        torch.cuda.synchronize()
+        return (h1 - h0) / n * 1e6
+    with torch.cuda.stream(stream):
+        host_fwd = host_us(lambda: A.attn_fwd(q, k, v, s, out, lse, window=wp.window,
+                                              scale=wp.scale, stream=stream))
+        host_dec = host_us(lambda: A.attn_decode_splitkv(qd, kd, vd, sl, ns, op, lp,
+                                                         window=wd.window, scale=wd.scale,
+                                                         stream=stream), n=10)
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -455,6 +472,9 @@ def main():
             "traffic": traffic,
             "kernel": "fwd_bf16_kernel<128,false,false,false>",
             "ms_per_launch": round(t_fwd.mean() * 1e3, 4),
+            "ms_median": round(float(np.median(t_fwd)) * 1e3, 4),
+            "ms_min": round(float(t_fwd.min()) * 1e3, 4),
+            "host_us_per_call": round(host_fwd, 1),
         },
         "decode": {
             "GB/s": round(dec_gbps, 1),
@@ -472,6 +492,9 @@ def main():
             "traffic": dec_traffic,
             "kernel": "decode_kernel<128,false>",
             "ms_per_launch": round(t_dec.mean() * 1e3, 4),
+            "ms_median": round(float(np.median(t_dec)) * 1e3, 4),
+            "ms_min": round(float(t_dec.min()) * 1e3, 4),
+            "host_us_per_call": round(host_dec, 1),
         },
     }
     if not args.step_only:
