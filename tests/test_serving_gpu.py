@@ -60,7 +60,7 @@ def run_paged(q, kp, vp, table, seqlens, nsplits, sinks, window, scale, max_spli
     return op.cpu().numpy(), lp.cpu().numpy(), out[:, :, 0].cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("page_size", [16, 64, 256])
+@pytest.mark.parametrize("page_size", [1, 8, 16, 64, 256, 1024])
 @pytest.mark.parametrize("window", [0, 513])
 def test_paged_decode(gpu, page_size, window):
     w = W.SPLITKV_DECODE
