@@ -15,6 +15,8 @@
 // Finalise: the sink logit joins with the rebased update of the Flint page
 // ("fix two"): m' = max(m, sink*log2e), r = 2^(m - m'),
 // l' = l*r + 2^(sink*log2e - m'), O = acc*r/l', LSE = ln2*(m' + log2 l').
+// A wave's 32-row Q block comes in, and its O block goes out, through LDS as
+// whole rows (copy_rows_to_lds, store_rows_staged).
 //
 // The float32-input variant is the same algorithm on v_mfma_f32_32x32x2_f32
 // with 128-row work-groups of one head, 32-key tiles, register-staged copies
