@@ -280,6 +280,38 @@ def cpu_baseline(w, q, k, v, sinks, budget_s=20.0):
             "sample": f"{done} of {w.Hq} heads of {w.name} (all rows), float64 numpy, {dt:.1f} s"}
 
 
+def cpu_baseline_decode(wd, q, kv, seqlens, nsplits, sinks, budget_s=8.0):
+    """Time the float64 oracle's split-KV decode + combine on whole sequences
+    (the first ones of the decode workload; kv[b] = their K, V rows) until
+    ~budget_s of work; rate in the GPU path's algorithmic bytes (bf16 K/V rows
+    + q + O + LSE)."""
+    import oracle
+    from exact_attention_attn_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    for b in range(len(kv)):
+        qb = W.as_float(q[b:b + 1], wd.dtype)
+        kb = W.as_float(kv[b][0], wd.dtype)
+        vb = W.as_float(kv[b][1], wd.dtype)
+        o_p, l_p, n_valid = oracle.decode_partials(qb, kb, vb, seqlens[b:b + 1], nsplits[b:b + 1],
+                                                   wd.window, wd.scale)
+        oracle.combine(o_p, l_p, n_valid, sinks)
+        done += 1
+        nbytes += decode_bytes(seqlens[b:b + 1], wd.Hq, wd.Hkv, wd.D, wd.window)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {q.shape[0]} sequences of {wd.name} "
+                      f"(sum Lk {int(np.asarray(seqlens[:done], np.int64).sum())}), "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +365,9 @@ def main():
     if args.keys_per_split > 0:
         nsplits = W.splits_policy(seqlens, args.keys_per_split)
     qd, kd, vd = up(dq, W.BF16), up(dk, W.BF16), up(dv, W.BF16)
+    # the first sequences' rows, kept for the oracle's decode timing
+    kv_host = [(dk[b:b + 1, :, :int(seqlens[b])].copy(), dv[b:b + 1, :, :int(seqlens[b])].copy())
+               for b in range(4)] if not args.no_cpu_baseline else []
     del dk, dv
     sl = torch.from_numpy(seqlens).to(dev)
     ns = torch.from_numpy(nsplits).to(dev)
@@ -509,6 +544,7 @@ def main():
         }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wp, qh, kh, vh, sh)
+        res["cpu_baseline_decode"] = cpu_baseline_decode(wd, dq, kv_host, seqlens, nsplits, dsinks)
     print(json.dumps(res), flush=True)
 
 
