@@ -206,7 +206,10 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&o)[D / 32], flo
   for (int i = 0; i < kRowsPerWave / RPI; ++i) {
     const int r = i * RPI + rr;
     const u32x4 v = lds_read16(stage, r * ROWB + ((cc ^ (r & (CH - 1))) << 4));
-    if (r < nrows) *(u32x4*)((char*)oblock + (size_t)r * ROWB + cc * 16) = v;
+    // Streaming stores: each output row is written once and not read back
+    // here; written through the caches they slow the K/V reads beside them.
+    if (r < nrows)
+      __builtin_nontemporal_store(v, (u32x4*)((char*)oblock + (size_t)r * ROWB + cc * 16));
   }
 }
 
