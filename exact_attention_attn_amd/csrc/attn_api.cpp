@@ -133,6 +133,7 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   if (B < 1 || Hq < 1 || Hkv < 1 || Lk_max < 1) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0 || max_splits < 1 || max_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
   if (!fits(B, Hkv, Lk_max, D) || !fits(B, Hq, max_splits, D)) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq * max_splits >= (1LL << 31)) return ATTN_ERR_SHAPE;  // 32-bit item ids
   if ((long long)B * Hq >= (1LL << 31) || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
   if (!supported_dim(D) || in_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!(std::isfinite(scale) && scale > 0.0f)) return ATTN_ERR_VALUE;
@@ -162,6 +163,7 @@ int attn_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_
   if (Lk_max >= (1LL << 31) || !fits(num_pages, Hkv, page_size, D) || !fits(B, Hq, max_splits, D) ||
       !fits(B, max_pages_per_seq, 1, 1))
     return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq * max_splits >= (1LL << 31)) return ATTN_ERR_SHAPE;  // 32-bit item ids
   if ((long long)B * Hq >= (1LL << 31) || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
   if (!supported_dim(D) || in_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!(std::isfinite(scale) && scale > 0.0f)) return ATTN_ERR_VALUE;

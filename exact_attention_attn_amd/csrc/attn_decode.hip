@@ -3,11 +3,11 @@
 // Decode: the work items are the splits of every (sequence, KV head,
 // query-column group).  The G = Hq/Hkv query heads that share a KV head are
 // the columns of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each K/V byte of a
-// split is read from HBM once for all of them.  The grid is persistent: each
-// work-group streams a contiguous range of items, 128-key tiles staged
-// through LDS, with the next tile (and, at an item's end, the next item's
-// first tile and Q) prefetched into registers while the current tile is
-// computed.  Wave w scores keys [32w, 32w+32) of every tile with its own
+// split is read from HBM once for all of them.  Each work-group streams a
+// contiguous range of items (about one with the launch's grid), 128-key
+// tiles staged through LDS, with the next tile (and, at an item's end, the
+// next item's first tile and Q) prefetched into registers while the current
+// tile is computed.  Wave w scores keys [32w, 32w+32) of every tile with its own
 // online-softmax state; at the end of an item the four states are merged
 // through LDS into the split's normalised partial output and sink-free LSE.
 //
@@ -19,6 +19,7 @@
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
+#include <algorithm>
 #include <atomic>
 
 namespace attn {
@@ -77,9 +78,9 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-// Persistent split-KV decode: work-group w of n streams items
-// [total*w/n, total*(w+1)/n) of the flat item list; the copy of the next tile
-// (possibly the next item's first) is in flight while a tile is computed.
+// Split-KV decode: each work-group streams a contiguous range of the flat
+// item list (its XCD's share, see below); the copy of the next tile (possibly
+// the next item's first) is in flight while a tile is computed.
 // PAGED: key j of sequence b is row j % page_size of page
 // table[b][j / page_size]; each lane looks up the pages of its rows (page ids
 // are clamped into the pool, so a bad table cannot address outside it).
@@ -105,40 +106,99 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   const int G = a.Hq / a.Hkv;
 
   // Total items and this work-group's range (every wave computes the same).
+  // The lengths and split counts of sequences 0 .. 255 are loaded in
+  // one round and kept in registers for both scans and the first item, so a
+  // work-group waits for one round trip before it can stream; later
+  // sequences are read again.
+  constexpr int kPre = 4;
+  int pre_sl[kPre], pre_ns[kPre], pre_n[kPre], pre_incl[kPre];
+  long long pre_chunk[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int b = 64 * j + lane;
+    pre_sl[j] = b < a.B ? a.seqlens[b] : 0;
+    pre_ns[j] = b < a.B ? a.nsplits[b] : 1;
+  }
   long long total = 0;
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const SplitRange sr = split_rule(pre_sl[j], pre_ns[j], a.Lk_max, a.max_splits, a.window);
+    pre_n[j] = 64 * j + lane < a.B ? sr.n_valid * a.Hkv * a.n_qgroups : 0;
+    pre_incl[j] = wave_incl_scan(pre_n[j], lane);
+    pre_chunk[j] = __builtin_amdgcn_readfirstlane(__shfl(pre_incl[j], 63));
+    total += pre_chunk[j];
+  }
+  for (int b0 = 64 * kPre; b0 < a.B; b0 += 64) {
     SplitRange sr;
     int n = (b0 + lane < a.B) ? items_of(a, b0 + lane, sr) : 0;
     total += __builtin_amdgcn_readfirstlane(__shfl(wave_incl_scan(n, lane), 63));
   }
-  const long long lo = total * blockIdx.x / gridDim.x;
-  const long long hi = total * (blockIdx.x + 1) / gridDim.x;
+  // Work-groups are dealt round-robin over the 8 XCDs.  Group x of the
+  // X = min(8, grid) groups (work-groups x, x + X, ...; one XCD each) takes an
+  // X-th of the items, its k-th work-group the k-th share of them: one item each, front-loaded in dispatch order, when there are no
+  // more items than work-groups (the rest exit at once), else contiguous
+  // ranges.
+  // Item counts fit in 32 bits: the host bounds B*Hq*max_splits below 2^31.
+  int lo, hi;
+  {
+    const int tot = (int)total;
+    const int X = min(8, (int)gridDim.x);
+    const int x = blockIdx.x % X, k = blockIdx.x / X;
+    const int m = gridDim.x / X + (x < (int)(gridDim.x % X) ? 1 : 0);
+    const int q8 = tot / X, r8 = tot % X;
+    const int x_lo = x * q8 + min(x, r8), t = q8 + (x < r8 ? 1 : 0);
+    if (t <= m) {
+      lo = x_lo + k;
+      hi = k < t ? lo + 1 : lo;
+    } else {
+      const int qq = t / m, rr = t % m;
+      lo = x_lo + k * qq + min(k, rr);
+      hi = lo + qq + (k < rr ? 1 : 0);
+    }
+  }
   if (lo >= hi) return;  // uniform over the work-group
   int items_left = (int)(hi - lo);
 
-  // Locate the first item: sequence b and index r within it.
-  int cur_b = 0, cur_r = 0;
+  // Locate the first item: sequence b and index r within it (the first lane
+  // whose inclusive prefix passes lo).
+  int cur_b = 0, cur_r = 0, cur_n = 0;
+  SplitRange cur_sr;
   {
     long long base = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 64) {
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      if (!found && base + pre_chunk[j] > lo) {
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(base + pre_incl[j] > lo);
+        const int l0 = __builtin_ctzll(m);
+        const int excl = __builtin_amdgcn_readlane(pre_incl[j] - pre_n[j], l0);
+        cur_b = 64 * j + l0;
+        cur_r = (int)(lo - base - excl);
+        cur_n = __builtin_amdgcn_readlane(pre_n[j], l0);
+        cur_sr = split_rule(__builtin_amdgcn_readlane(pre_sl[j], l0),
+                            __builtin_amdgcn_readlane(pre_ns[j], l0), a.Lk_max, a.max_splits,
+                            a.window);
+        found = true;
+      }
+      if (!found) base += pre_chunk[j];
+    }
+    for (int b0 = 64 * kPre; !found && b0 < a.B; b0 += 64) {
       SplitRange sr;
       int n = (b0 + lane < a.B) ? items_of(a, b0 + lane, sr) : 0;
       int incl = wave_incl_scan(n, lane);
       long long chunk = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
       if (base + chunk > lo) {
-        // first lane whose inclusive prefix passes lo
         unsigned long long m = __builtin_amdgcn_ballot_w64(base + incl > lo);
         int l0 = __builtin_ctzll(m);
         int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - n, l0));
         cur_b = b0 + l0;
         cur_r = (int)(lo - base - excl);
-        break;
+        cur_n = items_of(a, cur_b, cur_sr);
+        found = true;
       }
       base += chunk;
     }
   }
-  SplitRange cur_sr;
-  int cur_n = items_of(a, cur_b, cur_sr);
   Item it = make_item(a, cur_b, cur_r, cur_sr);
 
   // Advance to the next item (skipping sequences without keys).
@@ -607,9 +667,14 @@ hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v
   int G = Hq / Hkv;
   a.n_qgroups = (G + 31) / 32;
   a.c = scale * kLog2e;
-  // Persistent grid: two work-groups per compute unit, each streaming a
-  // contiguous range of the item list.
-  dim3 grid(2 * cu_count());
+  // Far more work-groups than fit at once (two per compute unit), so that
+  // the hardware hands the remaining items to whichever compute units are
+  // free: work-groups with equal shares finished up to 2x apart when each
+  // compute unit's two owned a fixed sixteenth of the items.  Capped at the
+  // most items the launch can have (splits beyond a sequence's count exit at
+  // once).
+  const long long max_items = (long long)B * Hkv * a.n_qgroups * max_splits;
+  dim3 grid((unsigned)std::min<long long>(32LL * cu_count(), max_items));
   const bool paged = block_table != nullptr;
   if (D == 128) {
     if (paged) hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);

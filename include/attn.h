@@ -52,8 +52,9 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
   ATTN_ERR_SHAPE = 2,       /* a size < 1 (Lq, Lk, B, heads), Hq % Hkv != 0,
-                               Lq > Lk, max_splits outside [1, 64], or an
-                               index space that overflows 64-bit offsets     */
+                               Lq > Lk, max_splits outside [1, 64], a decode
+                               with B*Hq*max_splits >= 2^31, or an index
+                               space that overflows 64-bit offsets           */
   ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64/128, unknown or unsupported dtype */
   ATTN_ERR_VALUE = 4,       /* scale not finite and > 0, or a misaligned pointer */
   ATTN_ERR_HIP = 5          /* the HIP runtime rejected a launch              */

@@ -99,6 +99,7 @@ def dec(lib, **kw):
     (dict(q=None), 1), (dict(sl=None), 1), (dict(ns=None), 1), (dict(op=None), 1), (dict(lp=None), 1),
     (dict(B=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(ms=0), 2), (dict(ms=65), 2), (dict(Lk=0), 2),
     (dict(D=80), 3), (dict(ind=1), 3), (dict(scale=0.0), 4), (dict(k=P + 4), 4), (dict(sl=P + 2), 4),
+    (dict(B=1 << 16, Hq=512, Hkv=512), 2),  # B*Hq*max_splits = 2^31: item ids need 32 bits
 ])
 def test_decode_rejects(lib, kw, code):
     assert dec(lib, **kw) == code
@@ -188,7 +189,7 @@ def paged(lib, **kw):
     (dict(B=0), 2), (dict(npg=0), 2), (dict(ps=0), 2), (dict(ps=24), 2), (dict(mp=0), 2),
     (dict(ms=65), 2), (dict(Hq=6, Hkv=4), 2), (dict(mp=1 << 27, ps=1 << 5), 2),
     (dict(D=80), 3), (dict(ind=1), 3), (dict(scale=-1.0), 4), (dict(bt=P + 2), 4),
-    (dict(kp=P + 8), 4),
+    (dict(kp=P + 8), 4), (dict(B=1 << 16, Hq=512, Hkv=512), 2),
 ])
 def test_paged_rejects(lib, kw, code):
     assert paged(lib, **kw) == code

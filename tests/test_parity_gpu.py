@@ -224,6 +224,49 @@ def test_decode_head_groups(gpu, G, D):
     check_decode(q, kc, vc, seqlens, np.array([3, 1, 64], np.int32), sinks, 0, f"G={G} D={D}")
 
 
+@pytest.mark.parametrize("B,max_splits", [(1, 1), (1, 3), (2, 3), (1, 5)])
+def test_decode_small_grids(gpu, B, max_splits):
+    # max_splits bounds the launch's work-groups (B * Hkv * max_splits here),
+    # so these run on 1 to 6 of them: fewer than the XCDs they are dealt to
+    rng = np.random.default_rng(B * 10 + max_splits)
+    Hq, Hkv, D, Lmax = 4, 1, 128, 900
+    seqlens = np.array([900, 131][:B], np.int32)
+    nsplits = np.array([max_splits, max(1, max_splits - 1)][:B], np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, 1, D), dtype=np.float32))
+    kc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 70 + max_splits, 1, lengths=seqlens)
+    vc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 70 + max_splits, 2, lengths=seqlens)
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    say(f"decode small grid B={B} max_splits={max_splits}")
+    op, lp, o, l = run_decode(q, kc, vc, seqlens, nsplits, sinks, 0, D ** -0.5, max_splits=max_splits)
+    op_r, lp_r, nv, o_r, l_r = decode_oracle(q, kc, vc, seqlens, nsplits, sinks, 0, D ** -0.5)
+    for b in range(B):
+        n = int(nv[b])
+        compare(op[b, :, :n], lp[b, :, :n], op_r[b, :, :n], lp_r[b, :, :n], f"small grid partials b={b}")
+        assert np.isnan(op[b, :, n:]).all() and np.isnan(lp[b, :, n:]).all()
+    compare(o, l, o_r, l_r, f"small grid B={B} max_splits={max_splits}")
+
+
+def test_decode_many_sequences(gpu):
+    # more sequences than the kernel keeps split counts of in registers (256)
+    rng = np.random.default_rng(300)
+    B, Hq, Hkv, D, Lmax = 300, 8, 2, 64, 200
+    seqlens = rng.integers(0, Lmax, size=B, endpoint=True).astype(np.int32)
+    nsplits = rng.integers(1, 6, size=B).astype(np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, 1, D), dtype=np.float32))
+    kc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 300, 1, lengths=seqlens)
+    vc = W.normal_tensor((B, Hkv, Lmax, D), W.BF16, 300, 2, lengths=seqlens)
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    say("decode B=300")
+    op, lp, o, l = run_decode(q, kc, vc, seqlens, nsplits, sinks, 0, D ** -0.5, max_splits=8)
+    op_r, lp_r, nv, o_r, l_r = decode_oracle(q, kc, vc, seqlens, nsplits, sinks, 0, D ** -0.5)
+    for b in range(B):
+        n = int(nv[b])
+        if n:
+            compare(op[b, :, :n], lp[b, :, :n], op_r[b, :, :n], lp_r[b, :, :n], f"B=300 partials b={b}")
+        assert np.isnan(op[b, :, n:]).all() and np.isnan(lp[b, :, n:]).all()
+    compare(o, l, o_r, l_r, "decode B=300")
+
+
 def test_decode_empty_sequence_and_no_sink(gpu):
     rng = np.random.default_rng(5)
     B, Hq, Hkv, D, Lmax = 3, 8, 1, 128, 256
