@@ -435,8 +435,12 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs
   }
 }
 
+// At most two waves per SIMD: the compiler then schedules with up to 256
+// registers (176 used) instead of fitting three waves in 160, and the backward
+// measured 3% faster on both the sliding-window and causal shapes.
 template <int D>
-__global__ __launch_bounds__(kBfThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdArgs a) {
   lds_char* Q0 = KvSmem<D>::template q<0>();
   lds_char* Q1 = KvSmem<D>::template q<1>();
   lds_char* G0 = KvSmem<D>::template g<0>();
