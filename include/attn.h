@@ -218,11 +218,12 @@ int attn_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_
  *                      per = ceil(I / S), with, for target c: I the decode's
  *                      work items (valid splits x Hkv x ceil((Hq/Hkv)/32)),
  *                      Z the largest split in keys, T = sum_b n_b x Hkv x
- *                      ceil((Hq/Hkv)/32) and S the decode's work-groups
- *                      (param, or 2 x compute units when param = 0).  The
- *                      first (smallest) such c wins.  The estimate is the
- *                      keys of the most loaded work-group plus a per-item
- *                      overhead of 96 key rows, both measured on MI355X.
+ *                      ceil((Hq/Hkv)/32) and S the decode's concurrent
+ *                      work-groups (param, or 2 x compute units when
+ *                      param = 0).  The first (smallest) such c wins.  The
+ *                      estimate is the keys of the most loaded of those
+ *                      slots plus a per-item overhead of 96 key rows, both
+ *                      measured on MI355X.
  * seqlens_k [B] int32 (device); num_splits [B] int32 (device, written).
  * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (sizes as in attn_decode_splitkv),
  * ATTN_ERR_UNSUPPORTED (unknown policy), ATTN_ERR_VALUE (param < 1 for
