@@ -33,6 +33,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 // (vmcnt = 0) and leaves the export and LDS counters unconstrained.
 constexpr int kWaitVmcnt0 = (7 << 4) | (0xF << 8);
 
+// Word 3 of a raw (unstructured) buffer resource on CDNA: 32-bit data format,
+// no swizzle, no stride.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // s_waitcnt immediate for vmcnt <= n (0 <= n < 64), other counters unconstrained.
 __host__ __device__ constexpr int wait_vmcnt_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8);

@@ -96,7 +96,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   constexpr int MERGE_BYTES = kWaves * 32 * (D + 4) * 4;
   __shared__ __attribute__((aligned(16))) char
       tile_raw[2 * TILE_BYTES > MERGE_BYTES ? 2 * TILE_BYTES : MERGE_BYTES];
-  __shared__ float sm_m[kWaves * 32], sm_l[kWaves * 32];
   lds_char* ks_ = (lds_char*)tile_raw;
   lds_char* vs_ = ks_ + TILE_BYTES;
 
@@ -409,8 +408,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
       // normalised partial output and its sink-free LSE, in one pass: once
       // every wave is done with this tile, its LDS holds the four waves'
       // unnormalised O columns ([wave][column] rows of D floats, padded by
-      // 16 B), and the next tile is stored only after the barrier at the top
-      // of the loop.
+      // 16 B that hold the column's max and sum), and the next tile is stored
+      // only after the barrier at the top of the loop.
       const float l_tot = pair_sum(l_run);
       const int n_cols = min(32, G - it.qg * 32);
       constexpr int NCH = D / 4;  // 16 B chunks per column
@@ -427,23 +426,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
                         __builtin_bit_cast(u32x4, (f32x4){o[db][j * 4], o[db][j * 4 + 1],
                                                           o[db][j * 4 + 2], o[db][j * 4 + 3]}));
           }
-        if (half == 0) {
-          sm_m[wave * 32 + col] = m_run;
-          sm_l[wave * 32 + col] = l_tot;
-        }
+        // the column's running max and partial sum go into the row's padding
+        if (half == 0)
+          lds_write8(sm, rbase + D * 4,
+                     (u32x2){__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_tot)});
       }
       __syncthreads();
       for (int idx = threadIdx.x; idx < n_cols * NCH; idx += kThreads) {
         const int cq = idx / NCH, ch = idx % NCH;
+        float mw[kWaves], lw[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const lds_char* pad = sm + (w * 32 + cq) * PITCH + D * 4;
+          mw[w] = *(const __attribute__((address_space(3))) float*)pad;
+          lw[w] = *(const __attribute__((address_space(3))) float*)(pad + 4);
+        }
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 32 + cq]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
         float L = 0.0f;
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float f = exp2_fast(sm_m[w * 32 + cq] - M);  // -inf (wave saw no key) -> 0
-          L += sm_l[w * 32 + cq] * f;
+          const float f = exp2_fast(mw[w] - M);  // -inf (wave saw no key) -> 0
+          L += lw[w] * f;
           const f32x4 x = __builtin_bit_cast(
               f32x4, lds_read16(sm, (w * 32 + cq) * PITCH + ch * 16));
 #pragma unroll

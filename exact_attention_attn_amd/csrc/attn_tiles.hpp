@@ -71,10 +71,6 @@ __device__ __forceinline__ uint32_t dma_src_off(int pc, int lane) {
   return (uint32_t)(r * L::kRow + c * 16);
 }
 
-// Word 3 of a raw (unstructured) buffer resource on CDNA: 32-bit data format,
-// no swizzle, no stride.
-constexpr int kRawBufferWord3 = 0x00020000;
-
 template <int D>
 struct TileCopy {
   using L = BfLayout<D>;
