@@ -37,6 +37,10 @@ constexpr int kWaitVmcnt0 = (7 << 4) | (0xF << 8);
 // no swizzle, no stride.
 constexpr int kRawBufferWord3 = 0x00020000;
 
+// Cache-policy operand of buffer loads and stores (gfx950): bit 0 sc0, bit 1
+// nt, bit 4 sc1.
+constexpr int kCpolSc1 = 16;
+
 // s_waitcnt immediate for vmcnt <= n (0 <= n < 64), other counters unconstrained.
 __host__ __device__ constexpr int wait_vmcnt_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8);
