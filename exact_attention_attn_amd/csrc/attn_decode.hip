@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombArgs a) {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanCands = 11;
 __constant__ int kPlanChunks[kPlanCands] = {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192};
-constexpr long long kPlanItemCost = 96;  // per-item overhead, in key rows
+constexpr long long kPlanItemCost = 80;  // per-item overhead, in key rows
 
 struct PlanArgs {
   const int32_t* seqlens;
@@ -715,7 +715,9 @@ hipError_t launch_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int
   a.B = B; a.Lk_max = Lk_max; a.max_splits = max_splits; a.window = window;
   a.policy = policy; a.param = param;
   // the decode's own grid: launch_decode runs 2 work-groups per compute unit
-  a.slots = (policy == ATTN_SPLITS_AUTO && param > 0) ? param : 2 * cu_count();
+  // The unit of throughput is the compute unit: one work-group per CU streams
+  // about as fast as two, and the items are spread over CUs.
+  a.slots = (policy == ATTN_SPLITS_AUTO && param > 0) ? param : cu_count();
   const int G = Hq / Hkv;
   a.hq = Hkv * ((G + 31) / 32);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);

@@ -214,16 +214,16 @@ int attn_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_
  *   ATTN_SPLITS_AUTO   num_splits[b] = ceil(n_b / c) for the chunk target c in
  *                      {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096,
  *                      6144, 8192} that minimises
- *                        min(per * Z, ceil(T / S) + Z) + 96 * per,
+ *                        min(per * Z, ceil(T / S) + Z) + 80 * per,
  *                      per = ceil(I / S), with, for target c: I the decode's
  *                      work items (valid splits x Hkv x ceil((Hq/Hkv)/32)),
  *                      Z the largest split in keys, T = sum_b n_b x Hkv x
- *                      ceil((Hq/Hkv)/32) and S the decode's concurrent
- *                      work-groups (param, or 2 x compute units when
+ *                      ceil((Hq/Hkv)/32) and S the units the items are
+ *                      spread over (param, or the compute units when
  *                      param = 0).  The first (smallest) such c wins.  The
- *                      estimate is the keys of the most loaded of those
- *                      slots plus a per-item overhead of 96 key rows, both
- *                      measured on MI355X.
+ *                      estimate is the keys of the most loaded unit plus a
+ *                      per-item overhead of 80 key rows, both fitted to
+ *                      measurements on MI355X.
  * seqlens_k [B] int32 (device); num_splits [B] int32 (device, written).
  * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (sizes as in attn_decode_splitkv),
  * ATTN_ERR_UNSUPPORTED (unknown policy), ATTN_ERR_VALUE (param < 1 for

@@ -347,7 +347,7 @@ def split_ranges(Lk: int, num_splits: int, window: int) -> list[tuple[int, int]]
 # include/attn.h, and restated here step by step.
 PLAN_COUNT, PLAN_KEYS, PLAN_AUTO = "count", "keys", "auto"
 PLAN_CHUNKS = (256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
-PLAN_ITEM_COST = 96  # per-item overhead of the decode, in key rows
+PLAN_ITEM_COST = 80  # per-item overhead of the decode, in key rows
 
 
 def visible_keys(seqlen: int, Lk_max: int, window: int) -> int:
@@ -367,8 +367,8 @@ def plan_splits(seqlens, Hq: int, Hkv: int, Lk_max: int, window: int, max_splits
     per = ceil(I / S), where for target c every sequence takes ceil(n/c)
     splits, I counts the decode's work items (valid splits x KV heads x
     query-column groups of 32), Z is the largest split in keys, T the visible
-    key rows times KV heads and groups, and S the number of work-groups the
-    decode runs (slots).  The first such c wins.  Splits are clamped to
+    key rows times KV heads and groups, and S the units the items are spread
+    over (slots).  The first such c wins.  Splits are clamped to
     [1, max_splits] in every policy.
     """
     ns_of = lambda n, c: min(max(-(-n // c), 1), max_splits)

@@ -266,7 +266,7 @@ def err_max_logit_gqa(seed=0, Hq=8, Hkv=2, L=30, D=8, window=5):
 # The planning rule as include/attn.h states it, retyped here on purpose so
 # that a changed constant in the oracle shows up.
 RULE_CHUNKS = (256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
-RULE_ITEM_COST = 96
+RULE_ITEM_COST = 80
 
 
 def brute_plan_auto(seqlens, Hq, Hkv, Lk_max, window, max_splits, slots):

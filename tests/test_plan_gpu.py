@@ -29,7 +29,7 @@ def device_plan(seqlens, Hq, Hkv, Lk_max, window, max_splits, policy, param):
 
 
 def decode_slots():
-    return 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    return torch.cuda.get_device_properties(0).multi_processor_count
 
 
 SHAPES = [  # (B, Lk_max, window, Hq, Hkv, max_splits)
