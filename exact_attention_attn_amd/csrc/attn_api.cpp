@@ -186,6 +186,7 @@ int attn_decode_plan(const int32_t* seqlens_k, int32_t* num_splits, int B, int H
   if (B < 1 || Hq < 1 || Hkv < 1 || Lk_max < 1) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0 || max_splits < 1 || max_splits > ATTN_MAX_SPLITS || B > 65535 || Hq > 65535)
     return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq * max_splits >= (1LL << 31)) return ATTN_ERR_SHAPE;  // 32-bit item counts
   if (policy != ATTN_SPLITS_AUTO && policy != ATTN_SPLITS_KEYS && policy != ATTN_SPLITS_COUNT)
     return ATTN_ERR_UNSUPPORTED;
   if (policy == ATTN_SPLITS_AUTO ? param < 0 : param < 1) return ATTN_ERR_VALUE;

@@ -560,12 +560,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombArgs a) {
 // ---------------------------------------------------------------------------
 // Split-count planning (attn_decode_plan).  One work-group; for the auto
 // policy every thread accumulates, over its sequences, the item count and the
-// largest split of each candidate chunk target, then thread 0 picks the
-// target of least estimated cost (rule stated in include/attn.h).
+// largest split of each candidate chunk target; threads 0..10 then price one
+// candidate each and thread 0 takes the first of least estimated cost (rule
+// stated in include/attn.h).  Item counts fit in 32 bits (the API bounds
+// B*Hq*max_splits below 2^31); dividing by the candidate targets, which are
+// compile-time constants, costs a multiply.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 256;
 constexpr int kPlanCands = 11;
-__constant__ int kPlanChunks[kPlanCands] = {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192};
+constexpr int kPlanChunks[kPlanCands] = {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192};
 constexpr long long kPlanItemCost = 80;  // per-item overhead, in key rows
 
 struct PlanArgs {
@@ -583,14 +586,14 @@ __device__ __forceinline__ int splits_for(int n, int target, int max_splits) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ long long s_items[kPlanCands][kPlanThreads / 64];
+  __shared__ int s_items[kPlanCands][kPlanThreads / 64];
   __shared__ int s_z[kPlanCands][kPlanThreads / 64];
   __shared__ long long s_T[kPlanThreads / 64];
+  __shared__ long long s_cost[kPlanCands];
   __shared__ int s_target;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (a.policy == ATTN_SPLITS_AUTO) {
-    long long items[kPlanCands];
-    int z[kPlanCands];
+    int items[kPlanCands], z[kPlanCands];
 #pragma unroll
     for (int i = 0; i < kPlanCands; ++i) { items[i] = 0; z[i] = 0; }
     long long T = 0;
@@ -621,23 +624,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       for (int i = 0; i < kPlanCands; ++i) { s_items[i][wave] = items[i]; s_z[i][wave] = z[i]; }
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < kPlanCands) {
       long long tot = 0;
-      for (int w = 0; w < kPlanThreads / 64; ++w) tot += s_T[w];
-      tot *= a.hq;
-      const long long S = a.slots;
-      long long best = -1;
-      int target = kPlanChunks[0];
-      for (int i = 0; i < kPlanCands; ++i) {
-        long long it = 0;
-        int zz = 0;
-        for (int w = 0; w < kPlanThreads / 64; ++w) { it += s_items[i][w]; zz = max(zz, s_z[i][w]); }
-        it *= a.hq;
-        const long long per = (it + S - 1) / S;
-        const long long cost = min(per * zz, (tot + S - 1) / S + zz) + kPlanItemCost * per;
-        if (best < 0 || cost < best) { best = cost; target = kPlanChunks[i]; }
+      int it = 0, zz = 0;
+#pragma unroll
+      for (int w = 0; w < kPlanThreads / 64; ++w) {
+        tot += s_T[w];
+        it += s_items[tid][w];
+        zz = max(zz, s_z[tid][w]);
       }
-      s_target = target;
+      tot *= a.hq;
+      it *= a.hq;
+      const unsigned S = (unsigned)a.slots;  // >= 1
+      const long long per = ((unsigned)it + S - 1u) / S;  // < 2^32: it < 2^31, S <= 2^31
+      const long long ts = (tot + S - 1) / S;
+      s_cost[tid] = min(per * zz, ts + zz) + kPlanItemCost * per;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int best = 0;
+      for (int i = 1; i < kPlanCands; ++i)
+        if (s_cost[i] < s_cost[best]) best = i;
+      s_target = kPlanChunks[best];
     }
     __syncthreads();
   }

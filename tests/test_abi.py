@@ -150,6 +150,7 @@ def plan(lib, **kw):
     (dict(ms=65), 2), (dict(Lk=0), 2), (dict(B=70000), 2), (dict(policy=3), 3), (dict(policy=-1), 3),
     (dict(policy=0, param=-1), 4), (dict(policy=1, param=0), 4), (dict(policy=2, param=0), 4),
     (dict(sl=P + 2), 4), (dict(ns=P + 1), 4),
+    (dict(B=1 << 15, Hq=1024, Hkv=1024), 2),  # B*Hq*max_splits = 2^31: item counts need 32 bits
 ])
 def test_plan_rejects(lib, kw, code):
     assert plan(lib, **kw) == code

@@ -44,7 +44,8 @@ def test_plan_matches_oracle(gpu, B, Lk_max, window, Hq, Hkv, max_splits):
     rng = np.random.default_rng(B + Lk_max)
     seqlens = rng.integers(-10, Lk_max + 500, B).tolist()
     say(f"plan B={B} Lk_max={Lk_max} W={window} H={Hq}/{Hkv} ms={max_splits}")
-    cases = [("auto", 0, decode_slots()), ("auto", 77, 77), ("auto", 512, 512), ("keys", 1, 0),
+    cases = [("auto", 0, decode_slots()), ("auto", 77, 77), ("auto", 512, 512),
+             ("auto", 2**31 - 1, 2**31 - 1), ("keys", 1, 0),
              ("keys", 100, 0), ("keys", 1024, 0), ("count", 1, 0), ("count", 5, 0), ("count", 100, 0)]
     for policy, param, slots in cases:
         got = device_plan(seqlens, Hq, Hkv, Lk_max, window, max_splits, policy, param)
