@@ -47,7 +47,7 @@ struct Row {
 // turn s into probabilities in place and return the rescale factor for acc.
 // With MAXL the exact running maximum of the raw scores is kept in row.mx
 // (row.m lags it by up to the rebase threshold).
-template <int N, bool MAXL>
+template <int N, bool MAXL, bool SUM = true>
 __device__ __forceinline__ float softmax_tile(float (&s)[N], Row& row, float c) {
   float mx = s[0];
 #pragma unroll
@@ -67,9 +67,9 @@ __device__ __forceinline__ float softmax_tile(float (&s)[N], Row& row, float c) 
 #pragma unroll
   for (int v = 0; v < N; ++v) {
     s[v] = exp2_fast(__builtin_fmaf(s[v], c, -m_use));
-    sum += s[v];
+    if (SUM) sum += s[v];
   }
-  row.l += sum;
+  if (SUM) row.l += sum;
   return alpha;
 }
 
@@ -206,12 +206,19 @@ template <int D, bool MAXL>
 __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* vs_,
                                           const int (&ka)[D / 16], const int (&va)[2][D / 32],
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
-                                          Row& row, int kind, int t0, int vis_lo, int vis_hi,
-                                          int half, float c) {
+                                          Row& row, float (&pend)[32], int kind, int t0,
+                                          int vis_lo, int vis_hi, int half, float c) {
   using L = BfLayout<D>;
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int KA = 4;  // K k-steps read ahead (both key blocks)
+
+  // The previous tile's probabilities join the row sum here, beside this
+  // tile's S^T MFMAs (the wave has no other VALU work there); the sum is
+  // formed in the same order as it would be right after the exponentials.
+  float prev = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 32; ++v) prev += pend[v];
 
   // S^T for key blocks 0 and 1, k-steps interleaved.
   f32x16 st0 = (f32x16){}, st1 = (f32x16){};
@@ -235,7 +242,11 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
   for (int ks = 0; ks < KS; ++ks) {
     if (ks + KA < KS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 32 / KS, 0);
   }
+  // Keep the sum in this block (it would otherwise sink past the mask branch).
+  asm volatile("" : "+v"(prev));
+  row.l += prev;
 
   // The first V operands of P V are read before the softmax, which hides
   // their LDS latency behind it.
@@ -268,7 +279,9 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
         s[kb * 16 + v] = (j - lo <= span) ? s[kb * 16 + v] : kNegInf;
       }
   }
-  float alpha = softmax_tile<32, MAXL>(s, row, c);
+  float alpha = softmax_tile<32, MAXL, false>(s, row, c);
+#pragma unroll
+  for (int v = 0; v < 32; ++v) pend[v] = s[v];
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] *= alpha;
@@ -381,6 +394,9 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
   Row row = {kNegInf, 0.0f, kNegInf};
+  float pend[32];  // probabilities of the last computed tile, not yet in row.l
+#pragma unroll
+  for (int v = 0; v < 32; ++v) pend[v] = 0.0f;
   const int p = my_row + off_q;
   int vis_hi = min(p, Lk - 1);
   int vis_lo = a.window > 0 ? p - a.window + 1 : 0;
@@ -410,12 +426,19 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     if (t + 1 < t_end) cp.issue(kh, vh, t + 1, Lk, kn, vn);
     const int kind = wave_active ? tile_kind(t * kBc, kBc, w_span, a.window, Lk) : 0;
     if (kind != 0)
-      bf16_tile<D, MAXL>(ks_, vs_, ka, va, qf, o, row, kind, t * kBc, vis_lo, vis_hi, half, a.c);
+      bf16_tile<D, MAXL>(ks_, vs_, ka, va, qf, o, row, pend, kind, t * kBc, vis_lo, vis_hi,
+                         half, a.c);
   };
   for (int t = t_begin; t < t_end; t += 2) {
     step(t, K0, V0, K1, V1);
     if (t + 1 >= t_end) break;
     step(t + 1, K1, V1, K0, V0);
+  }
+  {
+    float prev = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) prev += pend[v];
+    row.l += prev;
   }
 
   // O staging: with bf16 output a wave's block fits the stage that held tile

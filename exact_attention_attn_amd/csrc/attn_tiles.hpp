@@ -106,6 +106,7 @@ struct TileCopy {
 };
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002;
 constexpr int kSgMfma = 0x008;
 constexpr int kSgDsRead = 0x100;
 
