@@ -22,7 +22,10 @@ SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_api.cpp"]
 # accumulators in architectural VGPRs: the softmax rescales them with VALU
 # instructions, and accumulators in AGPRs would be copied back and forth
 # around that (rarely taken) branch on every tile.
-SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+# The forward is also built without NaN semantics: its inputs are finite
+# (infinities are still honoured: masked scores are -inf), and maxnum then
+# needs no canonicalising copies of its operands in the per-tile row maximum.
+SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
                 "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
