@@ -254,6 +254,66 @@ def measure_serving(A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dls
     return res
 
 
+def run_sweep(A, W, torch, dev):
+    """One JSON line per shape: attn_fwd TFLOP/s over sequence lengths, windows
+    and head dims, and split-KV decode + combine GB/s over batch/length mixes.
+    Inputs are seeded N(0, 1) values rounded to bf16, generated on the device."""
+    g = torch.Generator(device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device=dev).to(torch.bfloat16)
+
+    for D in (128, 64):
+        for L, B in ((1024, 8), (4096, 2), (16384, 1)):
+            Hq, Hkv = 64, 8
+            g.manual_seed(L + D)
+            q, k, v = rnd(B, Hq, L, D), rnd(B, Hkv, L, D), rnd(B, Hkv, L, D)
+            sk = torch.randn(Hq, generator=g, device=dev)
+            out = torch.empty_like(q)
+            lse = torch.empty(B, Hq, L, dtype=torch.float32, device=dev)
+            for Wn in (0, 129, 513, 2049):
+                if Wn >= L:
+                    continue
+                t = warm_then_time(torch, stream, lambda: A.attn_fwd(
+                    q, k, v, sk, out, lse, window=Wn, scale=D ** -0.5, stream=stream), 20)
+                fl = 4.0 * D * B * Hq * pairs_window(L, Wn)
+                print(json.dumps({"sweep": "attn_fwd", "B": B, "Hq": Hq, "Hkv": Hkv, "L": L,
+                                  "D": D, "window": Wn, "ms": round(t * 1e3, 4),
+                                  "TFLOP/s": round(fl / t / 1e12, 1),
+                                  "frac": round(fl / t / 2.5e15, 4)}), flush=True)
+            del q, k, v, out, lse
+            torch.cuda.empty_cache()
+    for D in (128, 64):
+        for B, lo, hi in ((8, 65536, 131072), (32, 8192, 32768), (128, 1024, 16384),
+                          (256, 512, 4096)):
+            Hq, Hkv, MS = 64, 8, 64
+            rng = np.random.default_rng([B, lo, D])
+            seqlens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+            nsplits = W.splits_policy(seqlens, 1024, MS)
+            g.manual_seed(B + D)
+            q, kc, vc = rnd(B, Hq, 1, D), rnd(B, Hkv, hi, D), rnd(B, Hkv, hi, D)
+            sk = torch.randn(Hq, generator=g, device=dev)
+            sl, ns = torch.from_numpy(seqlens).to(dev), torch.from_numpy(nsplits).to(dev)
+            op = torch.empty(B, Hq, MS, D, dtype=torch.float32, device=dev)
+            lp = torch.empty(B, Hq, MS, dtype=torch.float32, device=dev)
+            out = torch.empty(B, Hq, 1, D, dtype=torch.bfloat16, device=dev)
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+
+            def both():
+                A.attn_decode_splitkv(q, kc, vc, sl, ns, op, lp, scale=D ** -0.5, stream=stream)
+                A.attn_combine(op, lp, sl, ns, sk, out, lse, Lk_max=hi, stream=stream)
+            t = warm_then_time(torch, stream, both, 10)
+            nb = decode_bytes(seqlens, Hq, Hkv, D, 0)
+            print(json.dumps({"sweep": "decode+combine", "B": B, "Hq": Hq, "Hkv": Hkv,
+                              "Lk": [lo, hi], "sum_Lk": int(seqlens.sum()), "D": D,
+                              "splits": int(nsplits.sum()), "ms": round(t * 1e3, 4),
+                              "GB/s": round(nb / t / 1e9, 1), "frac": round(nb / t / 8e12, 4)}),
+                  flush=True)
+            del q, kc, vc, op, lp
+            torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, q, k, v, sinks, budget_s=20.0):
     """Time the float64 oracle on whole heads of the prefill until ~budget_s of work."""
     import oracle
@@ -329,6 +389,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: attn_fwd and decode rates over a range of shapes, "
+                         "one JSON line each")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
@@ -345,6 +408,9 @@ def main():
         sys.exit(1)
     A.load_library()
     dev = torch.device("cuda", 0)
+    if args.sweep:
+        run_sweep(A, W, torch, dev)
+        return
 
     def up(x, dtype):
         if dtype == W.BF16:
