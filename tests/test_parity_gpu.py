@@ -116,6 +116,22 @@ def test_fewer_queries_than_keys(gpu, Lq, Lk, window):
     compare(o, l, o_ref, l_ref, f"Lq={Lq} Lk={Lk} W={window}")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(6, 2), (12, 4), (16, 1), (10, 5), (32, 2)])
+def test_head_group_shapes(gpu, Hq, Hkv):
+    # G = 3 and 5 (one query head per wave group), 16 (four groups of four
+    # heads per KV head), 2 with an odd KV-head count.
+    rng = np.random.default_rng(Hq * 13 + Hkv)
+    D, Lq, Lk = 128, 170, 300
+    q = W.f32_to_bf16_bits(rng.standard_normal((1, Hq, Lq, D), dtype=np.float32))
+    k = W.f32_to_bf16_bits(rng.standard_normal((1, Hkv, Lk, D), dtype=np.float32))
+    v = W.f32_to_bf16_bits(rng.standard_normal((1, Hkv, Lk, D), dtype=np.float32))
+    sinks = rng.normal(0.0, 2.0, Hq).astype(np.float32)
+    for window in (0, 100):
+        o, l = run_fwd(q, k, v, sinks, W.BF16, window, D ** -0.5)
+        o_ref, l_ref = full_oracle(q, k, v, sinks, W.BF16, window, D ** -0.5)
+        compare(o, l, o_ref, l_ref, f"H={Hq}/{Hkv} W={window}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_no_sink_and_large_scores(gpu, D):
     rng = np.random.default_rng(D)
