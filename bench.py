@@ -433,7 +433,7 @@ def main():
     qd, kd, vd = up(dq, W.BF16), up(dk, W.BF16), up(dv, W.BF16)
     # the first sequences' rows, kept for the oracle's decode timing
     kv_host = [(dk[b:b + 1, :, :int(seqlens[b])].copy(), dv[b:b + 1, :, :int(seqlens[b])].copy())
-               for b in range(4)] if not args.no_cpu_baseline else []
+               for b in range(16)] if not args.no_cpu_baseline else []
     del dk, dv
     sl = torch.from_numpy(seqlens).to(dev)
     ns = torch.from_numpy(nsplits).to(dev)
