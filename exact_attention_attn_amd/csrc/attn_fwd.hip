@@ -10,7 +10,8 @@
 //                   edge or the end of the keys
 //   online softmax  in the exp2 domain (running max m, partial sum l); the
 //                   accumulator is rebased only when the max grew by > 8
-//                   (2^8 headroom keeps every term finite in fp32)
+//                   (2^8 headroom keeps every term finite in fp32); a tile's
+//                   probabilities join l beside the next tile's S^T MFMAs
 //   O^T += V^T P^T  V read from LDS with ds_read_b64_tr_b16, P in bf16 (RNE)
 // Finalise: the sink logit joins with the rebased update of the Flint page
 // ("fix two"): m' = max(m, sink*log2e), r = 2^(m - m'),
