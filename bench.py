@@ -191,6 +191,24 @@ def measure_backward(A, torch, dev, stream, q, k, v, s, wp, reps=10):
                     "recomputes S and dP (14*D per pair executed)"}
 
 
+def combine_bytes(seqlens, nsplits, Hq, D, window, max_splits=64) -> int:
+    """Bytes the combine must move: the valid splits' partial O rows (fp32) and
+    LSEs, read, plus the bf16 O and fp32 LSE written.  The valid split count of
+    a sequence follows the split rule of include/attn.h: per = ceil(n / ns),
+    chunk = per rounded up to 64 keys, n_valid = ceil(n / chunk)."""
+    total = 0
+    for n, ns in zip(np.asarray(seqlens, np.int64), np.asarray(nsplits, np.int64)):
+        n = min(int(n), window) if window > 0 else int(n)
+        ns = min(max(int(ns), 1), max_splits)
+        if n <= 0:
+            continue
+        per = -(-n // ns)
+        chunk = -(-per // 64) * 64
+        total += -(-n // chunk)
+    B = len(seqlens)
+    return total * Hq * (D + 1) * 4 + B * Hq * D * 2 + B * Hq * 4
+
+
 def pairs_window(L: int, W: int) -> int:
     """Unmasked (query, key) pairs of one head: sum_i min(i + 1, W) (W <= 0: causal)."""
     if W <= 0 or W >= L:
@@ -538,6 +556,7 @@ def main():
     flops = wp.flops()
     tflops = flops / t_fwd.mean() / 1e12
     dbytes = decode_bytes(seqlens, wd.Hq, wd.Hkv, wd.D, wd.window)
+    comb_bytes = combine_bytes(seqlens, nsplits, wd.Hq, wd.D, wd.window)
     dec_gbps = dbytes / (t_dec.mean() + t_cmb.mean()) / 1e9
     traffic = stored_traffic("fwd_bf16_kernel<128,false,false,false>:" + wp.name)
     dec_traffic = stored_traffic("decode_kernel<128,false>:" + wd.name)
@@ -582,7 +601,10 @@ def main():
             "frac_hbm": round(dec_gbps / PEAK_HBM_GBPS, 4),
             "decode_ms": round(t_dec.mean() * 1e3, 4),
             "combine_ms": round(t_cmb.mean() * 1e3, 4),
-            "note": "GB/s = algorithmic bytes (visible K/V rows + q + O + LSE) / (decode + combine time)",
+            "combine_GB/s": round(comb_bytes / t_cmb.mean() / 1e9, 1),
+            "combine_bytes": comb_bytes,
+            "note": "GB/s = algorithmic bytes (visible K/V rows + q + O + LSE) / (decode + combine time); "
+                    "combine_GB/s = (valid partial O rows and LSEs read + O and LSE written) / combine time",
         },
         "roofline_decode": {
             "bound": "hbm",
