@@ -34,3 +34,19 @@ def test_decode_and_combine_bytes_follow_the_split_rule(window):
     rows = sum(min(int(n), window) if window > 0 else int(n) for n in seqlens)
     want_dec = rows * Hkv * D * 2 * 2 + 2 * B * Hq * D * 2 + B * Hq * 4 + Hq * 4
     assert bench.decode_bytes(seqlens, Hq, Hkv, D, window) == want_dec
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # One process per GPU is the only mode: --gpus above 1 ends with an error
+    # line before anything touches a device.
+    import json
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    line = json.loads(res.stdout.strip().splitlines()[-1])
+    assert "one GPU" in line["error"] and line["n_gpus"] == 2
