@@ -14,8 +14,8 @@ import os
 import threading
 
 __all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_bwd", "attn_decode_splitkv",
-           "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine", "attn_strerror", "AttnError",
-           "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
+           "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine", "attn_strerror",
+           "AttnError", "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
 
 ATTN_BF16 = 0
 ATTN_F32 = 1
@@ -99,6 +99,13 @@ def _dev(t, name: str, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def _same_dtype(q, **others):
+    """Only q's element type reaches the C ABI: the other inputs must share it."""
+    for name, t in others.items():
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
 
 
 def _stream(stream):
@@ -195,6 +202,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, out, lse=None, *
         raise ValueError("sinks must be [Hq]")
     if lse is not None and tuple(lse.shape) != (Hq, total_q):
         raise ValueError("lse must be [Hq,total_q]")
+    _same_dtype(q, k=k, v=v)
     if scale is None:
         scale = D ** -0.5
     rc = load_library().attn_fwd_varlen(
@@ -225,6 +233,7 @@ def attn_decode_splitkv_paged(q, k_pages, v_pages, block_table, seqlens_k, num_s
         raise ValueError("block_table must be [B,max_pages]")
     if tuple(o_part.shape) != (B, Hq, max_splits, D) or tuple(lse_part.shape) != (B, Hq, max_splits):
         raise ValueError("o_part must be [B,Hq,max_splits,D] and lse_part [B,Hq,max_splits]")
+    _check_decode_inputs(q, k_pages, v_pages, seqlens_k, num_splits)
     if scale is None:
         scale = D ** -0.5
     rc = load_library().attn_decode_splitkv_paged(
@@ -258,6 +267,7 @@ def attn_bwd(q, k, v, sinks, out, dout, lse, dq, dk, dv, dsink=None, delta=None,
         raise ValueError("sinks must be [Hq]")
     if dsink is not None and tuple(dsink.shape) != (Hq,):
         raise ValueError("dsink must be [Hq]")
+    _same_dtype(q, k=k, v=v)
     if delta is None:
         delta = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
     if scale is None:
@@ -270,6 +280,20 @@ def attn_bwd(q, k, v, sinks, out, dout, lse, dq, dk, dv, dsink=None, delta=None,
         B, Hq, Hkv, Lq, Lk, D, int(window), float(scale), _dtype_code(q), _dtype_code(out),
         _stream(stream))
     _check("attn_bwd", rc)
+
+
+def _check_decode_inputs(q, k_cache, v_cache, seqlens_k, num_splits):
+    """What the C ABI cannot check from pointers: element types of the cache
+    and per-sequence arrays of exactly B int32 (the kernels read B of each)."""
+    import torch
+
+    B = q.shape[0]
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    for name, t in (("seqlens_k", seqlens_k), ("num_splits", num_splits)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,):
+            raise ValueError(f"{name} must be int32 of shape ({B},), got {t.dtype} {tuple(t.shape)}")
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_part, *,
@@ -290,6 +314,7 @@ def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_
         raise ValueError("k_cache and v_cache shapes differ")
     if tuple(o_part.shape) != (B, Hq, max_splits, D) or tuple(lse_part.shape) != (B, Hq, max_splits):
         raise ValueError("o_part must be [B,Hq,max_splits,D] and lse_part [B,Hq,max_splits]")
+    _check_decode_inputs(q, k_cache, v_cache, seqlens_k, num_splits)
     if scale is None:
         scale = D ** -0.5
     rc = load_library().attn_decode_splitkv(
@@ -338,9 +363,17 @@ def attn_combine(o_part, lse_part, seqlens_k, num_splits, sinks, out, lse=None, 
         raise ValueError("out must be [B,Hq,1,D]")
     if lse is not None and tuple(lse.shape) != (B, Hq):
         raise ValueError("lse must be [B,Hq]")
+    if tuple(lse_part.shape) != (B, Hq, max_splits):
+        raise ValueError("lse_part must be [B,Hq,max_splits]")
+    for name, t in (("seqlens_k", seqlens_k), ("num_splits", num_splits)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,):
+            raise ValueError(f"{name} must be int32 of shape ({B},)")
+    if sinks is not None and tuple(sinks.shape) != (Hq,):
+        raise ValueError("sinks must be [Hq]")
     rc = load_library().attn_combine(
         _dev(o_part, "o_part", torch.float32), _dev(lse_part, "lse_part", torch.float32),
         _dev(seqlens_k, "seqlens_k", torch.int32), _dev(num_splits, "num_splits", torch.int32),
         _dev(sinks, "sinks", torch.float32), _dev(out, "out"), _dev(lse, "lse", torch.float32),
         B, Hq, D, int(Lk_max), max_splits, int(window), _dtype_code(out), _stream(stream))
     _check("attn_combine", rc)
+

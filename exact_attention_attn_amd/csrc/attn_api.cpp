@@ -51,6 +51,36 @@ int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 }  // namespace
 
+namespace attn {
+
+int check_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                 const int32_t* num_splits, int B, int Hq, int Hkv, int Lk_max, int D,
+                 int max_splits, float scale, int in_dtype) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !num_splits) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lk_max < 1) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || max_splits < 1 || max_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
+  if (!fits(B, Hkv, Lk_max, D) || !fits(B, Hq, max_splits, D)) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq * max_splits >= (1LL << 31)) return ATTN_ERR_SHAPE;  // 32-bit item ids
+  if ((long long)B * Hq >= (1LL << 31) || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+  if (!supported_dim(D) || in_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return ATTN_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) || (reinterpret_cast<uintptr_t>(num_splits) & 3u))
+    return ATTN_ERR_VALUE;
+  return ATTN_OK;
+}
+
+int check_combine_outputs(const float* sinks, const void* out, const float* lse, int out_dtype) {
+  if (!out) return ATTN_ERR_NULL;
+  if (!dtype_ok(out_dtype)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
+      (sinks && (reinterpret_cast<uintptr_t>(sinks) & 3u)))
+    return ATTN_ERR_VALUE;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
 extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, const float* sinks, void* out,
@@ -128,19 +158,11 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seqlens_k, const int32_t* num_splits, float* o_part,
                         float* lse_part, int B, int Hq, int Hkv, int Lk_max, int D,
                         int max_splits, int window, float scale, int in_dtype, void* stream) {
-  if (!q || !k_cache || !v_cache || !seqlens_k || !num_splits || !o_part || !lse_part)
-    return ATTN_ERR_NULL;
-  if (B < 1 || Hq < 1 || Hkv < 1 || Lk_max < 1) return ATTN_ERR_SHAPE;
-  if (Hq % Hkv != 0 || max_splits < 1 || max_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
-  if (!fits(B, Hkv, Lk_max, D) || !fits(B, Hq, max_splits, D)) return ATTN_ERR_SHAPE;
-  if ((long long)B * Hq * max_splits >= (1LL << 31)) return ATTN_ERR_SHAPE;  // 32-bit item ids
-  if ((long long)B * Hq >= (1LL << 31) || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
-  if (!supported_dim(D) || in_dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (!(std::isfinite(scale) && scale > 0.0f)) return ATTN_ERR_VALUE;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) ||
-      (reinterpret_cast<uintptr_t>(lse_part) & 3u) || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) ||
-      (reinterpret_cast<uintptr_t>(num_splits) & 3u))
-    return ATTN_ERR_VALUE;
+  if (!o_part || !lse_part) return ATTN_ERR_NULL;
+  const int rc = attn::check_decode(q, k_cache, v_cache, seqlens_k, num_splits, B, Hq, Hkv, Lk_max,
+                                    D, max_splits, scale, in_dtype);
+  if (rc != ATTN_OK) return rc;
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u)) return ATTN_ERR_VALUE;
   return from_hip(attn::launch_decode(q, k_cache, v_cache, seqlens_k, num_splits, o_part, lse_part,
                                       B, Hq, Hkv, Lk_max, D, max_splits, window, scale,
                                       static_cast<hipStream_t>(stream)));

@@ -117,6 +117,17 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return r;
 }
 
+// acc + the sum of the 8 bf16 values of v, in a fixed order (v_dot2c_f32_bf16
+// against (1, 1): each pair is added exactly, the sum rounds as fp32 adds do).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[e]), one, acc, false);
+  return acc;
+}
+
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   bf16x2 p = __builtin_convertvector((f32x2){a, b}, bf16x2);
   return __builtin_bit_cast(uint32_t, p);

@@ -297,7 +297,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
   const int tr_d = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
   f32x16 o[NDB];
-  float m_run = kNegInf, l_run = 0.0f;
+  // l_run sums the fp32 probabilities (for the LSE), lb_run the same values
+  // as rounded to bf16 for P V (the partial output's normaliser, so that a
+  // dominant key's rounding cancels).
+  float m_run = kNegInf, l_run = 0.0f, lb_run = 0.0f;
 
   int t0 = it.k_begin;
   load_q(it);
@@ -317,6 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
       for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
       m_run = kNegInf;
       l_run = 0.0f;
+      lb_run = 0.0f;
     }
     // Prefetch the next tile: of this item, or the first of the next item.
     const bool last = t0 + kTileKeys >= it.k_end;
@@ -374,6 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
         float alpha = need ? exp2_fast(m_run - m_new) : 1.0f;
         m_run = need ? m_new : m_run;
         l_run *= alpha;
+        lb_run *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] *= alpha;
       }
@@ -391,6 +396,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
         const float* x = sv + s2 * 8;
         pf[s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
       }
+      lb_run += sum_bf16x8(pf[1], sum_bf16x8(pf[0], 0.0f));
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -411,6 +417,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
       // 16 B that hold the column's max and sum), and the next tile is stored
       // only after the barrier at the top of the loop.
       const float l_tot = pair_sum(l_run);
+      const float lb_tot = pair_sum(lb_run);
       const int n_cols = min(32, G - it.qg * 32);
       constexpr int NCH = D / 4;  // 16 B chunks per column
       constexpr int PITCH = (D + 4) * 4;
@@ -426,30 +433,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
                         __builtin_bit_cast(u32x4, (f32x4){o[db][j * 4], o[db][j * 4 + 1],
                                                           o[db][j * 4 + 2], o[db][j * 4 + 3]}));
           }
-        // the column's running max and partial sum go into the row's padding
+        // the column's running max and its two partial sums go into the row's padding
         if (half == 0)
-          lds_write8(sm, rbase + D * 4,
-                     (u32x2){__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_tot)});
+          lds_write16(sm, rbase + D * 4,
+                      (u32x4){__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_tot),
+                              __builtin_bit_cast(uint32_t, lb_tot), 0u});
       }
       __syncthreads();
       for (int idx = threadIdx.x; idx < n_cols * NCH; idx += kThreads) {
         const int cq = idx / NCH, ch = idx % NCH;
-        float mw[kWaves], lw[kWaves];
+        float mw[kWaves], lw[kWaves], lbw[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const lds_char* pad = sm + (w * 32 + cq) * PITCH + D * 4;
           mw[w] = *(const __attribute__((address_space(3))) float*)pad;
           lw[w] = *(const __attribute__((address_space(3))) float*)(pad + 4);
+          lbw[w] = *(const __attribute__((address_space(3))) float*)(pad + 8);
         }
         float M = kNegInf;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
-        float L = 0.0f;
+        float L = 0.0f, Lb = 0.0f;
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const float f = exp2_fast(mw[w] - M);  // -inf (wave saw no key) -> 0
           L += lw[w] * f;
+          Lb += lbw[w] * f;
           const f32x4 x = __builtin_bit_cast(
               f32x4, lds_read16(sm, (w * 32 + cq) * PITCH + ch * 16));
 #pragma unroll
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
           const int hstride = a.max_splits * D * 4;  // bytes between heads
           const __amdgpu_buffer_rsrc_t prow = __builtin_amdgcn_make_buffer_rsrc(
               (void*)(a.o_part + row0 * D), 0, (64 / NCH - 1) * hstride + D * 4, kRawBufferWord3);
-          const f32x4 res = {acc[0] / L, acc[1] / L, acc[2] / L, acc[3] / L};
+          const f32x4 res = {acc[0] / Lb, acc[1] / Lb, acc[2] / Lb, acc[3] / Lb};
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, res), prow,
                                                  (cq - cq0) * hstride + ch * 16, 0, kCpolSc1);
         }

@@ -8,14 +8,17 @@
 //                   each lane owns one query column and 32 keys of it
 //   mask            only on tiles that cut the causal diagonal, the window
 //                   edge or the end of the keys
-//   online softmax  in the exp2 domain (running max m, partial sum l); the
+//   online softmax  in the exp2 domain (running max m, partial sums); the
 //                   accumulator is rebased only when the max grew by > 8
 //                   (2^8 headroom keeps every term finite in fp32); a tile's
-//                   probabilities join l beside the next tile's S^T MFMAs
-//   O^T += V^T P^T  V read from LDS with ds_read_b64_tr_b16, P in bf16 (RNE)
+//                   fp32 probabilities join l beside the next tile's S^T MFMAs
+//   O^T += V^T P^T  V read from LDS with ds_read_b64_tr_b16, P in bf16 (RNE);
+//                   the rounded P are summed too (lb), since a lazily rebased
+//                   dominant p lies in [1, 2^8) and its rounding (up to 2^-8
+//                   relative) must cancel between O's numerator and normaliser
 // Finalise: the sink logit joins with the rebased update of the Flint page
-// ("fix two"): m' = max(m, sink*log2e), r = 2^(m - m'),
-// l' = l*r + 2^(sink*log2e - m'), O = acc*r/l', LSE = ln2*(m' + log2 l').
+// ("fix two"): m' = max(m, sink*log2e), r = 2^(m - m'), e = 2^(sink*log2e - m'),
+// O = acc*r/(lb*r + e), LSE = ln2*(m' + log2(l*r + e)).
 // A wave's 32-row Q block comes in, and its O block goes out, through LDS as
 // whole rows (copy_rows_to_lds, store_rows_staged).
 //
@@ -40,8 +43,9 @@ constexpr float kRebaseThreshold = 8.0f;    // log2 headroom before the accumula
 // Online-softmax state of the query column a lane owns.
 struct Row {
   float m;   // reference max (log2 domain) of acc and l; -inf before any visible key
-  float l;   // partial sum of this lane half
+  float l;   // partial sum of this lane half (fp32 probabilities: the LSE's)
   float mx;  // largest raw score <q, k> seen (kept only when the max logit is asked for)
+  float lb;  // partial sum of the probabilities as rounded to bf16 for P V (O's normaliser)
 };
 
 // Update the running state with a tile of raw scores s (already masked to -inf),
@@ -62,6 +66,7 @@ __device__ __forceinline__ float softmax_tile(float (&s)[N], Row& row, float c) 
     alpha = need ? exp2_fast(row.m - m_new) : 1.0f;
     row.m = need ? m_new : row.m;
     row.l *= alpha;
+    row.lb *= alpha;
   }
   float m_use = row.m == kNegInf ? 0.0f : row.m;
   float sum = 0.0f;
@@ -113,18 +118,23 @@ __device__ __forceinline__ void finalize_store(const f32x16 (&o)[NDB], Row row, 
 
 // Finalise with the sink and store the wave's block of 32 consecutive output
 // rows (staged through LDS, see store_rows_staged) and the LSE.
+// The accumulator holds sum_j bf16(p_j) v_j, so O is normalised by the sum of
+// the same rounded p_j (a dominant key's rounding then cancels); the LSE takes
+// the fp32 sum.  The sink has no value vector and joins both unrounded.
 template <int D, typename OutT>
 __device__ __forceinline__ void finalize_store_rows(const f32x16 (&o)[D / 32], Row row,
                                                     float sink_l2, lds_char* stage, OutT* oblock,
                                                     int nrows, float* lse_dst, int col, int half,
                                                     int lane) {
   float l_tot = pair_sum(row.l);
+  float lb_tot = pair_sum(row.lb);
   float m_fin = fmaxf(row.m, sink_l2);
   float scale_o = 0.0f, lse = kNegInf;
   if (m_fin != kNegInf) {
     float r = exp2_fast(row.m - m_fin);  // row.m = -inf (no key) -> 0
-    float den = l_tot * r + exp2_fast(sink_l2 - m_fin);
-    scale_o = r / den;
+    float e_sink = exp2_fast(sink_l2 - m_fin);
+    float den = l_tot * r + e_sink;
+    scale_o = r / (lb_tot * r + e_sink);
     lse = (m_fin + log2_fast(den)) * kLn2;
   }
   store_rows_staged<D, OutT>(o, scale_o, stage, oblock, nrows, col, half, lane);
@@ -295,6 +305,14 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
       const float* x = s + kb * 16 + s2 * 8;
       pf[kb][s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
+  {
+    float sb = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) sb = sum_bf16x8(pf[kb][s2], sb);
+    row.lb += sb;
+  }
 
   // O^T += V^T P^T: step (kb, s2) feeds the D/32 independent accumulators.
 #pragma unroll
@@ -394,7 +412,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
-  Row row = {kNegInf, 0.0f, kNegInf};
+  Row row = {kNegInf, 0.0f, kNegInf, 0.0f};
   float pend[32];  // probabilities of the last computed tile, not yet in row.l
 #pragma unroll
   for (int v = 0; v < 32; ++v) pend[v] = 0.0f;
@@ -505,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
-  Row row = {kNegInf, 0.0f, kNegInf};
+  Row row = {kNegInf, 0.0f, kNegInf, 0.0f};
   const int p = my_row + off_q;
   const int vis_hi = min(p, a.Lk - 1);
   const int vis_lo = a.window > 0 ? p - a.window + 1 : 0;

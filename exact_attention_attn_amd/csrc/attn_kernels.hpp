@@ -6,6 +6,14 @@
 
 namespace attn {
 
+// Host-side argument checks shared by the entry points (ATTN_* codes).
+// check_decode: everything attn_decode_splitkv checks except its workspace
+// pointers; check_combine_outputs: attn_combine's sinks, out and lse.
+int check_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                 const int32_t* num_splits, int B, int Hq, int Hkv, int Lk_max, int D,
+                 int max_splits, float scale, int in_dtype);
+int check_combine_outputs(const float* sinks, const void* out, const float* lse, int out_dtype);
+
 // max_row / max_head (either may be NULL): largest pre-softmax logit per row
 // [B,Hq,Lq] and per head [B,Hq]; max_head is filled with -inf on the stream
 // first, then raised with atomics.

@@ -114,3 +114,32 @@ def run_decode(q, kc, vc, seqlens, nsplits, sinks, window, scale, max_splits=64,
     torch.cuda.synchronize()
     return (op.cpu().numpy(), lp.cpu().numpy(), out[:, :, 0].float().cpu().numpy(),
             lse.cpu().numpy())
+
+
+def run_decode_repeated(q, kc, vc, seqlens, nsplits, sinks, window, scale, repeats=5,
+                        max_splits=64):
+    """attn_decode_splitkv + attn_combine `repeats` times on the same device
+    inputs, buffers re-poisoned with NaN before each run; host copies of
+    (partials O, partials LSE, O, LSE) per run."""
+    qd, kd, vd = to_dev(q, W.BF16), to_dev(kc, W.BF16), to_dev(vc, W.BF16)
+    B, Hq, _, D = q.shape
+    sl = torch.from_numpy(np.asarray(seqlens, np.int32)).cuda()
+    ns = torch.from_numpy(np.asarray(nsplits, np.int32)).cuda()
+    sd = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
+    op = torch.empty((B, Hq, max_splits, D), dtype=torch.float32, device="cuda")
+    lp = torch.empty((B, Hq, max_splits), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Hq, 1, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    res = []
+    for _ in range(repeats):
+        op.fill_(float("nan"))
+        lp.fill_(float("nan"))
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        A.attn_decode_splitkv(qd, kd, vd, sl, ns, op, lp, window=window, scale=scale)
+        A.attn_combine(op, lp, sl, ns, sd, out, lse, Lk_max=kc.shape[2], window=window)
+        torch.cuda.synchronize()
+        res.append((op.cpu().numpy(), lp.cpu().numpy(), out[:, :, 0].cpu().numpy(),
+                    lse.cpu().numpy()))
+    del qd, kd, vd, op, lp, out, lse
+    return res

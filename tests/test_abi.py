@@ -214,3 +214,48 @@ def bwd(lib, **kw):
 ])
 def test_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def test_binding_checks_decode_inputs_on_host():
+    # Only pointers reach the C ABI, so the binding checks what it cannot:
+    # bf16 caches and per-sequence arrays of exactly B int32 (the kernels read B).
+    import torch
+
+    B, Hq, Hkv, L, D = 3, 4, 2, 16, 64
+    q = torch.zeros(B, Hq, 1, D, dtype=torch.bfloat16)
+    kc = torch.zeros(B, Hkv, L, D, dtype=torch.bfloat16)
+    sl = torch.full((B,), L, dtype=torch.int32)
+    op = torch.zeros(B, Hq, 8, D)
+    lp = torch.zeros(B, Hq, 8)
+    out = torch.zeros(B, Hq, 1, D)
+    with pytest.raises(TypeError):
+        A.attn_decode_splitkv(q, kc.float(), kc, sl, sl, op, lp)
+    with pytest.raises(ValueError):
+        A.attn_decode_splitkv(q, kc, kc, sl[:2], sl, op, lp)
+    with pytest.raises(ValueError):
+        A.attn_decode_splitkv(q, kc, kc, sl, sl.long(), op, lp)
+    with pytest.raises(ValueError):
+        A.attn_combine(op, lp, sl[:1], sl, None, out, Lk_max=L)
+    with pytest.raises(ValueError):
+        A.attn_combine(op, lp, sl, sl.float(), None, out, Lk_max=L)
+    pages = torch.zeros(6, Hkv, 8, D, dtype=torch.bfloat16)
+    table = torch.zeros(B, 2, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        A.attn_decode_splitkv_paged(q, pages.float(), pages, table, sl, sl, op, lp)
+    with pytest.raises(ValueError):
+        A.attn_decode_splitkv_paged(q, pages, pages, table, sl, sl[:1], op, lp)
+
+
+def test_binding_checks_input_dtypes_on_host():
+    import torch
+
+    q = torch.zeros(4, 10, 64, dtype=torch.bfloat16)
+    k = torch.zeros(2, 10, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(TypeError):
+        A.attn_fwd_varlen(q, k.float(), k, cu, cu, None, q.clone(), max_seqlen_q=10)
+    q4 = torch.zeros(1, 4, 10, 64, dtype=torch.bfloat16)
+    k4 = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16)
+    f = torch.zeros(1, 4, 10, 64)
+    with pytest.raises(TypeError):
+        A.attn_bwd(q4, k4, k4.float(), None, f, q4, torch.zeros(1, 4, 10), f, f[:, :2], f[:, :2])
