@@ -104,33 +104,44 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Pack 8 floats to bf16 (round to nearest even, v_cvt_pk_bf16_f32).
-__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
-                                              float a5, float a6, float a7) {
-  bf16x2 p0 = __builtin_convertvector((f32x2){a0, a1}, bf16x2);
-  bf16x2 p1 = __builtin_convertvector((f32x2){a2, a3}, bf16x2);
-  bf16x2 p2 = __builtin_convertvector((f32x2){a4, a5}, bf16x2);
-  bf16x2 p3 = __builtin_convertvector((f32x2){a6, a7}, bf16x2);
-  bf16x8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-// acc + the sum of the 8 bf16 values of v, in a fixed order (v_dot2c_f32_bf16
-// against (1, 1): each pair is added exactly, the sum rounds as fp32 adds do).
-__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
-  const u32x4 u = __builtin_bit_cast(u32x4, v);
-  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[e]), one, acc, false);
-  return acc;
-}
-
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   bf16x2 p = __builtin_convertvector((f32x2){a, b}, bf16x2);
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Pack 8 floats to bf16 (round to nearest even, v_cvt_pk_bf16_f32), as four
+// 32-bit words of two values each (first value in the low half).
+__device__ __forceinline__ u32x4 pack_bf16_words(float a0, float a1, float a2, float a3, float a4,
+                                                 float a5, float a6, float a7) {
+  return (u32x4){pack2_bf16(a0, a1), pack2_bf16(a2, a3), pack2_bf16(a4, a5), pack2_bf16(a6, a7)};
+}
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                              float a5, float a6, float a7) {
+  return __builtin_bit_cast(bf16x8, pack_bf16_words(a0, a1, a2, a3, a4, a5, a6, a7));
+}
+
+// Sums of bf16 values packed two to a 32-bit word (first value in the low
+// half), added to acc in a fixed order by v_dot2c_f32_bf16 against (1, 1):
+// each pair is added exactly, the running sum rounds as fp32 adds do.
+// The instructions are written as inline asm because the builtin, given words
+// held in a register tuple, lost their sub-register index (every dot product
+// read the tuple's first register).  A VALU instruction that reads the result
+// of a dot instruction needs 3 wait states on this chip; the compiler cannot
+// see that inside asm, so each block ends with them (s_nop 2).  Consecutive
+// dot2c instructions accumulating into the same register need none.
+__device__ __forceinline__ float sum_bf16_words(u32x4 a, u32x4 b, float acc) {
+  asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %2\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %3\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %4\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %5\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %6\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %7\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %8\n\t"
+      "s_nop 2"
+      : "+v"(acc)
+      : "v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w), "v"(b.x), "v"(b.y), "v"(b.z), "v"(b.w));
+  return acc;
 }
 
 // ---------------------------------------------------------------------------

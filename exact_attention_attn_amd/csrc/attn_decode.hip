@@ -391,12 +391,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
       }
       l_run += sum;
       bf16x8 pf[2];
+      u32x4 pw[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const float* x = sv + s2 * 8;
-        pf[s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+        pw[s2] = pack_bf16_words(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+        pf[s2] = __builtin_bit_cast(bf16x8, pw[s2]);
       }
-      lb_run += sum_bf16x8(pf[1], sum_bf16x8(pf[0], 0.0f));
+      lb_run = sum_bf16_words(pw[0], pw[1], lb_run);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -298,21 +298,16 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
     for (int db = 0; db < NDB; ++db) o[db] *= alpha;
   }
   bf16x8 pf[2][2];
+  u32x4 pw[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const float* x = s + kb * 16 + s2 * 8;
-      pf[kb][s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+      pw[kb][s2] = pack_bf16_words(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+      pf[kb][s2] = __builtin_bit_cast(bf16x8, pw[kb][s2]);
     }
-  {
-    float sb = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) sb = sum_bf16x8(pf[kb][s2], sb);
-    row.lb += sb;
-  }
+  row.lb = sum_bf16_words(pw[1][0], pw[1][1], sum_bf16_words(pw[0][0], pw[0][1], row.lb));
 
   // O^T += V^T P^T: step (kb, s2) feeds the D/32 independent accumulators.
 #pragma unroll
