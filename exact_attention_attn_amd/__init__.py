@@ -14,12 +14,14 @@ import os
 import threading
 
 __all__ = ["attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_bwd", "attn_decode_splitkv",
-           "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine", "attn_strerror",
-           "AttnError", "library_path", "load_library", "ATTN_BF16", "ATTN_F32", "MAX_SPLITS"]
+           "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine", "attn_decode_noalloc",
+           "attn_strerror", "AttnError", "library_path", "load_library", "ATTN_BF16", "ATTN_F32",
+           "MAX_SPLITS", "NOALLOC_SCRATCH_BYTES"]
 
 ATTN_BF16 = 0
 ATTN_F32 = 1
 MAX_SPLITS = 64
+NOALLOC_SCRATCH_BYTES = 135266304  # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
 SPLITS_POLICIES = {"auto": 0, "keys": 1, "count": 2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +42,7 @@ _SIGNATURES = {
     "attn_fwd_varlen": [_vp] * 8 + [_i] * 8 + [_f, _i, _i, _vp],
     "attn_bwd": [_vp] * 12 + [_i] * 7 + [_f, _i, _i, _vp],
     "attn_decode_splitkv_paged": [_vp] * 8 + [_i] * 9 + [_f, _i, _vp],
+    "attn_decode_noalloc": [_vp] * 8 + [_i] * 7 + [_f, _i, _i, _vp],
     "attn_strerror": [_i],
     "attn_version": [],
 }
@@ -377,3 +380,39 @@ def attn_combine(o_part, lse_part, seqlens_k, num_splits, sinks, out, lse=None, 
         B, Hq, D, int(Lk_max), max_splits, int(window), _dtype_code(out), _stream(stream))
     _check("attn_combine", rc)
 
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens_k, num_splits, sinks, out, lse=None, *,
+                        max_splits: int = MAX_SPLITS, window: int = 0, scale: float | None = None,
+                        stream=None) -> None:
+    """attn_decode_splitkv + attn_combine in one call that allocates nothing:
+    the split workspace is the library's fixed device array (NOALLOC_SCRATCH_BYTES;
+    larger workloads raise AttnError with code 6).  Calls that overlap in time
+    on one GPU share that array and race.
+
+    q [B,Hq,1,D] bf16; caches [B,Hkv,Lk_max,D] bf16; seqlens_k, num_splits [B]
+    int32; sinks [Hq] fp32 or None; out [B,Hq,1,D] (bf16 or fp32); lse [B,Hq] or None.
+    """
+    import torch
+
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query per sequence: q must be [B,Hq,1,D]")
+    _, Hkv, Lk_max, _ = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache shapes differ")
+    _check_decode_inputs(q, k_cache, v_cache, seqlens_k, num_splits)
+    if tuple(out.shape) != (B, Hq, 1, D):
+        raise ValueError("out must be [B,Hq,1,D]")
+    if lse is not None and tuple(lse.shape) != (B, Hq):
+        raise ValueError("lse must be [B,Hq]")
+    if sinks is not None and tuple(sinks.shape) != (Hq,):
+        raise ValueError("sinks must be [Hq]")
+    if scale is None:
+        scale = D ** -0.5
+    rc = load_library().attn_decode_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(seqlens_k, "seqlens_k", torch.int32), _dev(num_splits, "num_splits", torch.int32),
+        _dev(sinks, "sinks", torch.float32), _dev(out, "out"), _dev(lse, "lse", torch.float32),
+        B, Hq, Hkv, Lk_max, D, int(max_splits), int(window), float(scale), _dtype_code(q),
+        _dtype_code(out), _stream(stream))
+    _check("attn_decode_noalloc", rc)

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_noalloc.hip", "attn_api.cpp"]
 # Per-source code-generation options.  The forward kernel keeps its MFMA
 # accumulators in architectural VGPRs: the softmax rescales them with VALU
 # instructions, and accumulators in AGPRs would be copied back and forth

@@ -244,6 +244,8 @@ const char* attn_strerror(int code) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, dtype or policy";
     case ATTN_ERR_VALUE: return "invalid value (scale, policy parameter or pointer alignment)";
     case ATTN_ERR_HIP: return "HIP launch failed";
+    case ATTN_ERR_SCRATCH:
+      return "split workspace larger than the library's fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

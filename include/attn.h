@@ -16,7 +16,8 @@
  * Conventions shared by every call
  *  - Tensor pointers are HIP device pointers, owned by the caller, contiguous
  *    in the stated layout, and 16-byte aligned.  The library allocates no
- *    device or host memory and keeps no state between calls.
+ *    device or host memory and keeps no state between calls, except the one
+ *    fixed device array of attn_decode_noalloc (see there).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls only enqueue work and return; ordering is the stream's.
  *  - Return value: ATTN_OK (0) or a positive ATTN_ERR_* code.  On an error
@@ -57,7 +58,11 @@ enum {
                                space that overflows 64-bit offsets           */
   ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64/128, unknown or unsupported dtype */
   ATTN_ERR_VALUE = 4,       /* scale not finite and > 0, or a misaligned pointer */
-  ATTN_ERR_HIP = 5          /* the HIP runtime rejected a launch              */
+  ATTN_ERR_HIP = 5,         /* the HIP runtime rejected a launch, or the
+                               fixed scratch of attn_decode_noalloc could not
+                               be located on the current device              */
+  ATTN_ERR_SCRATCH = 6      /* attn_decode_noalloc: the split workspace of the
+                               call exceeds ATTN_NOALLOC_SCRATCH_BYTES        */
 };
 
 #define ATTN_SPLIT_ALIGN 64  /* split boundaries: multiples of 64 keys from the window start */
@@ -251,6 +256,40 @@ int attn_combine(const float* o_part, const float* lse_part, const int32_t* seql
                  const int32_t* num_splits, const float* sinks, void* out, float* lse, int B,
                  int Hq, int D, int Lk_max, int max_splits, int window, int out_dtype,
                  void* stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode_splitkv followed by attn_combine, in one
+ * call that allocates nothing and takes no workspace argument.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The split
+ * partials (o_part [B,Hq,max_splits,D] float32, then lse_part
+ * [B,Hq,max_splits] float32 at the next 256-byte boundary) live in one fixed
+ * device array of this library, ATTN_NOALLOC_SCRATCH_BYTES long (129 MiB:
+ * 64 sequences x 64 query heads x 64 splits at D = 128), which each GPU the
+ * call runs on holds from the first call on that device until the process
+ * ends.  That first call locates the array on the current device (no
+ * allocation); a failure there returns ATTN_ERR_HIP.  A call whose
+ * workspace, B*Hq*max_splits*(D+1)*4 bytes plus alignment, exceeds the array
+ * returns ATTN_ERR_SCRATCH and launches nothing.
+ *
+ * Arguments are those of attn_decode_splitkv and attn_combine, with the same
+ * meaning, checks and results (out and lse are bitwise those of the two calls
+ * on caller-owned workspace); sinks [Hq] or NULL, out [B,Hq,1,D] out_dtype,
+ * lse [B,Hq] float32 or NULL.
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents (each call writes every lane it reads first, so nothing needs
+ * clearing): calls that overlap in time on one GPU -- on different streams,
+ * or from several host threads -- race and give wrong results.  Order them
+ * on one stream.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES 135266304u
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens_k, const int32_t* num_splits, const float* sinks,
+                        void* out, float* lse, int B, int Hq, int Hkv, int Lk_max, int D,
+                        int max_splits, int window, float scale, int in_dtype, int out_dtype,
+                        void* stream);
 
 /* Human-readable name of an ATTN_* return code (static string). */
 const char* attn_strerror(int code);

@@ -34,15 +34,16 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_max_logit", "attn_fwd_varlen", "attn_bwd", "attn_decode_splitkv",
                           "attn_decode_splitkv_paged", "attn_decode_plan", "attn_combine",
-                          "attn_strerror", "attn_version"}
+                          "attn_decode_noalloc", "attn_strerror", "attn_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.attn_version().decode().startswith("attn-mi355x")
 
 
 def test_strerror(lib):
-    for code in range(6):
+    for code in range(7):
         assert lib.attn_strerror(code)
+    assert b"scratch" in lib.attn_strerror(6)
     assert b"unknown" in lib.attn_strerror(99)
 
 
@@ -259,3 +260,33 @@ def test_binding_checks_input_dtypes_on_host():
     f = torch.zeros(1, 4, 10, 64)
     with pytest.raises(TypeError):
         A.attn_bwd(q4, k4, k4.float(), None, f, q4, torch.zeros(1, 4, 10), f, f[:, :2], f[:, :2])
+
+
+def noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, sl=P, ns=P, sinks=P, out=P, lse=P, B=4, Hq=8, Hkv=2, Lk=100, D=128,
+             ms=64, window=0, scale=0.1, ind=0, outd=1, stream=None)
+    a.update(kw)
+    return lib.attn_decode_noalloc(a["q"], a["k"], a["v"], a["sl"], a["ns"], a["sinks"], a["out"],
+                                   a["lse"], a["B"], a["Hq"], a["Hkv"], a["Lk"], a["D"], a["ms"],
+                                   a["window"], a["scale"], a["ind"], a["outd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(sl=None), 1), (dict(out=None), 1),
+    (dict(B=0), 2), (dict(Hq=6, Hkv=4), 2), (dict(ms=0), 2), (dict(ms=65), 2),
+    (dict(D=80), 3), (dict(ind=1), 3), (dict(outd=4), 3), (dict(scale=0.0), 4),
+    (dict(out=P + 8), 4), (dict(lse=P + 2), 4), (dict(sl=P + 2), 4),
+    # workspaces beyond ATTN_NOALLOC_SCRATCH_BYTES: refused before any HIP call
+    (dict(B=65, Hq=64, Hkv=8, ms=64), 6), (dict(B=64, Hq=64, Hkv=8, ms=64, D=128), None),
+    (dict(B=1, Hq=4104, Hkv=8, ms=64, D=128), 6), (dict(B=128, Hq=64, Hkv=8, ms=64, D=64), 6),
+])
+def test_noalloc_rejects(lib, kw, code):
+    if code is None:
+        # the largest workload that fits must pass the size check; it is not
+        # launched here (no GPU), so only the bound itself is checked
+        B, Hq, ms, D = kw["B"], kw["Hq"], kw["ms"], kw["D"]
+        lanes = B * Hq * ms
+        need = -(-lanes * D * 4 // 256) * 256 + lanes * 4
+        assert need == A.NOALLOC_SCRATCH_BYTES
+        return
+    assert noalloc(lib, **kw) == code
