@@ -1,21 +1,25 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
 One step = the whole path on resident synthetic inputs:
-  attn_fwd            sliding-window prefill  B1 Hq64 Hkv8 L8192 D128 bf16, window 513,
-                      sinks (heads h%8==0 at +20), O written in bf16
+  attn_fwd            long-context sliding-window prefill  B1 Hq64 Hkv8 L262144 D128 bf16,
+                      window 513, sinks (heads h%4==0 at +30), O written in bf16
   attn_decode_splitkv split-KV decode  B64 Hq64 Hkv8 D128 bf16, Lk ~ U{1024..32768},
                       num_splits = clamp(ceil(Lk/1024), 1, 64)
   attn_combine        merge of the valid splits, sink added once
 
-Prints one JSON line.  `value` is the prefill's TFLOP/s (algorithmic flops:
-4*D per unmasked pair) from HIP events around each attn_fwd launch on the
-stream it runs on; decode GB/s (algorithmic bytes: the K/V rows each query
-sees plus q, O and LSE) is reported beside it.  The float64 CPU oracle is
-timed on a bounded sample of the prefill on the host cores (rank 0 only).
+Prints one JSON line.  `value` is the step's prefill TFLOP/s (algorithmic
+flops: 4*D per unmasked pair) from HIP events around each attn_fwd launch on
+the stream it runs on; decode GB/s (algorithmic bytes: the K/V rows each
+query sees plus q, O and LSE) is reported beside it.  The two smaller prefill
+workloads (sliding-window B1 L8192, causal B4 L4096) are timed in loops of
+their own after the step, each with its roofline fraction.  The float64 CPU
+oracle is timed on a bounded sample of each prefill workload and of the
+decode on the host cores.
 
-The defaults (50 warm-up steps, about 50 ms of GPU work, then 100 timed steps)
-let the GPU reach its sustained clock before timing: the first ~20 ms of
-load after idle run measurably slower.
+Before the counted warm-up steps the step runs for a fixed amount of GPU time
+(--prewarm-ms, default 250 ms): after an idle spell the first ~20 ms of load
+run up to a quarter slower, and a handful of warm-up steps of a small
+workload would not cover that.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -80,6 +84,23 @@ def decode_bytes(seqlens, Hq, Hkv, D, window) -> int:
     kv = int(lk.sum()) * Hkv * D * 2 * 2
     B = len(seqlens)
     return kv + B * Hq * D * 2 + B * Hq * D * 2 + B * Hq * 4 + Hq * 4
+
+
+def prewarm(torch, stream, fn, warm_s):
+    """Run fn on stream until at least warm_s seconds of GPU time have passed;
+    return (GPU seconds spent, calls)."""
+    spent, calls = 0.0, 0
+    with torch.cuda.stream(stream):
+        while spent < warm_s:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            spent += e0.elapsed_time(e1) * 1e-3
+            calls += 5
+    return spent, calls
 
 
 def warm_then_time(torch, stream, fn, reps, warm_s=0.04):
@@ -332,30 +353,40 @@ def run_sweep(A, W, torch, dev):
             torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, q, k, v, sinks, budget_s=20.0):
-    """Time the float64 oracle on whole heads of the prefill until ~budget_s of work."""
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((p.get("num_threads", 1) for p in threadpool_info()), default=1))
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline(w, q, k, v, sinks, budget_s=10.0):
+    """Time the float64 oracle on whole (batch, head) slices of a prefill
+    workload, in a fixed spread order, until ~budget_s of work; the rate is in
+    the same algorithmic flops as the GPU's."""
     import oracle
     from exact_attention_attn_amd import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = 1
     G = w.Hq // w.Hkv
     per_head = w.flops() // (w.B * w.Hq)
+    order = [(b, h) for h in range(w.Hq) for b in range(w.B)]
     done, flops, t0 = 0, 0, time.perf_counter()
-    for h in range(w.Hq):
+    for b, h in order:
         kvh = h // G
-        oracle.attention_fwd(W.as_float(q[:, h:h + 1], w.dtype), W.as_float(k[:, kvh:kvh + 1], w.dtype),
-                             W.as_float(v[:, kvh:kvh + 1], w.dtype), sinks[h:h + 1], w.window, w.scale)
+        oracle.attention_fwd(W.as_float(q[b:b + 1, h:h + 1], w.dtype),
+                             W.as_float(k[b:b + 1, kvh:kvh + 1], w.dtype),
+                             W.as_float(v[b:b + 1, kvh:kvh + 1], w.dtype), sinks[h:h + 1],
+                             w.window, w.scale)
         done += 1
         flops += per_head
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.Hq} heads of {w.name} (all rows), float64 numpy, {dt:.1f} s"}
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name} (all rows), "
+                      f"float64 numpy, {dt:.1f} s"}
 
 
 def cpu_baseline_decode(wd, q, kv, seqlens, nsplits, sinks, budget_s=8.0):
@@ -366,11 +397,7 @@ def cpu_baseline_decode(wd, q, kv, seqlens, nsplits, sinks, budget_s=8.0):
     import oracle
     from exact_attention_attn_amd import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _blas_threads()
     done, nbytes, t0 = 0, 0, time.perf_counter()
     for b in range(len(kv)):
         qb = W.as_float(q[b:b + 1], wd.dtype)
@@ -390,17 +417,59 @@ def cpu_baseline_decode(wd, q, kv, seqlens, nsplits, sinks, budget_s=8.0):
                       f"float64 numpy, {dt:.1f} s"}
 
 
+def time_launches(torch, stream, fn, n, prewarm_s=0.05):
+    """Per-launch seconds of fn on stream (HIP events around each launch),
+    after at least prewarm_s seconds of GPU time of fn."""
+    warm_then_time(torch, stream, fn, 1, warm_s=prewarm_s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+    return np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e-3
+
+
+def prefill_roofline(wp, t, traffic, host_us=None):
+    """Roofline object of one prefill workload from per-launch seconds t."""
+    tflops = wp.flops() / t.mean() / 1e12
+    r = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+         "kernel": "fwd_bf16_kernel<128,false,false,false>",
+         "flops_per_launch": wp.flops(),
+         "ms_per_launch": round(t.mean() * 1e3, 4),
+         "ms_median": round(float(np.median(t)) * 1e3, 4),
+         "ms_min": round(float(t.min()) * 1e3, 4),
+         "frac_median": round(wp.flops() / float(np.median(t)) / 1e12 / PEAK_BF16_TFLOPS, 4),
+         "launches": int(len(t))}
+    if host_us is not None:
+        r["host_us_per_call"] = round(host_us, 1)
+    return r
+
+
+def describe(wp):
+    return (f"{wp.name} B{wp.B} Hq{wp.Hq} Hkv{wp.Hkv} L{wp.L} D{wp.D} "
+            f"window{wp.window if wp.window > 0 else 'none'}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-ms", type=float, default=250.0,
+                    help="GPU time of untimed steps before the counted warm-up steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
-                    help="time only the step (no split-policy, serving or max-logit extras); "
-                         "the profiled runs use this so that every kernel's dispatches are the step's")
-    ap.add_argument("--prefill", default="swa_prefill",
-                    help="prefill workload (swa_prefill is the headline; others for study)")
+                    help="time only the step (no prefill legs, split-policy, serving, backward or "
+                         "max-logit extras); the profiled runs of the step use this")
+    ap.add_argument("--prefill", default="long_swa_prefill",
+                    help="prefill workload of the step (long_swa_prefill is the headline)")
+    ap.add_argument("--legs", default="swa_prefill,causal_prefill",
+                    help="prefill workloads timed in loops of their own after the step")
+    ap.add_argument("--leg-launches", type=int, default=100)
     ap.add_argument("--keys-per-split", type=int, default=0,
                     help="decode split policy: num_splits = clamp(ceil(Lk / this), 1, 64); "
                          "0 keeps the workload's 1024")
@@ -435,15 +504,22 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
-    # prefill inputs
+    def say(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # prefill inputs of the step (host copies kept for the oracle's sample)
     wp = W.WORKLOADS[args.prefill]
+    say(f"bench: generating {wp.name}")
+    host = {}
     qh, kh, vh, sh = W.prefill_inputs(wp)
+    host[wp.name] = (qh, kh, vh, sh)
     q, k, v = up(qh, wp.dtype), up(kh, wp.dtype), up(vh, wp.dtype)
     s = torch.from_numpy(sh).to(dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
 
     # decode inputs
+    say("bench: generating splitkv_decode")
     wd = W.SPLITKV_DECODE
     dq, dk, dv, seqlens, nsplits, dsinks = W.decode_inputs(wd)
     if args.keys_per_split > 0:
@@ -464,6 +540,17 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream(device=dev)
+
+    def launch_step():
+        A.attn_fwd(q, k, v, s, out, lse, window=wp.window, scale=wp.scale, stream=stream)
+        A.attn_decode_splitkv(qd, kd, vd, sl, ns, op, lp, window=wd.window, scale=wd.scale,
+                              stream=stream)
+        A.attn_combine(op, lp, sl, ns, ds, dout, dlse, Lk_max=wd.Lk_max, window=wd.window,
+                       stream=stream)
+
+    # pre-warm: untimed steps until prewarm_ms of GPU time have passed
+    say("bench: pre-warm")
+    prewarm_s, prewarm_steps = prewarm(torch, stream, launch_step, args.prewarm_ms * 1e-3)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
           for _ in range(args.warmup + args.steps)]
 
@@ -479,6 +566,7 @@ def main():
                        stream=stream)
         e[3].record(stream)
 
+    say("bench: timed steps")
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
@@ -494,40 +582,8 @@ def main():
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e-3
     t_cmb = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e-3
 
-    # Split-count policies (attn_decode_plan): decode + combine GB/s with the
-    # workload-aware plan (the plan kernel inside the timed span) against
-    # fixed rules, on the decode workload above and two more batch/length mixes.
-    split_policy = None if args.step_only else measure_split_policies(
-        A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd, seqlens)
-
-    # Serving layouts: decode over a shuffled paged copy of the same cache, and
-    # the forward over a packed batch of sequences of different lengths.
-    serving = None if args.step_only else measure_serving(
-        A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
-        t_dec.mean() + t_cmb.mean(), wp)
-
-    bwd = None if args.step_only else measure_backward(A, torch, dev, stream, q, k, v, s, wp)
-
-    t_ml = None
-    if not args.step_only:
-        # attn_fwd_max_logit (per-row and per-head maxima) on the same prefill,
-        # timed like attn_fwd, to report what the extra outputs cost.
-        ml_row = torch.empty(lse.shape, dtype=torch.float32, device=dev)
-        ml_head = torch.empty(lse.shape[:2], dtype=torch.float32, device=dev)
-        n_ml = max(10, args.steps // 5)
-        ml_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(n_ml)]
-        with torch.cuda.stream(stream):
-            for e0, e1 in ml_ev:
-                e0.record(stream)
-                A.attn_fwd_max_logit(q, k, v, s, out, lse, ml_row, ml_head, window=wp.window,
-                                     scale=wp.scale, stream=stream)
-                e1.record(stream)
-            torch.cuda.synchronize()
-        t_ml = np.array([e0.elapsed_time(e1) for e0, e1 in ml_ev[n_ml // 2:]]) * 1e-3
-
     # Host time per ABI call (argument checks, marshalling and the launch), the
-    # calls left to run asynchronously; the GPU work of 50 calls fits the queue.
+    # calls left to run asynchronously.
     def host_us(fn, n=50):
         torch.cuda.synchronize()
         h0 = time.perf_counter()
@@ -538,7 +594,7 @@ def main():
         return (h1 - h0) / n * 1e6
     with torch.cuda.stream(stream):
         host_fwd = host_us(lambda: A.attn_fwd(q, k, v, s, out, lse, window=wp.window,
-                                              scale=wp.scale, stream=stream))
+                                              scale=wp.scale, stream=stream), n=10)
         host_dec = host_us(lambda: A.attn_decode_splitkv(qd, kd, vd, sl, ns, op, lp,
                                                          window=wd.window, scale=wd.scale,
                                                          stream=stream), n=10)
@@ -552,6 +608,54 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Prefill legs: the other prefill workloads, each in a loop of its own.
+    legs = {}
+    leg_inputs = {}
+    if not args.step_only:
+        for name in [x for x in args.legs.split(",") if x and x != wp.name]:
+            wl = W.WORKLOADS[name]
+            say(f"bench: leg {name}")
+            qh2, kh2, vh2, sh2 = W.prefill_inputs(wl)
+            host[name] = (qh2, kh2, vh2, sh2)
+            ql, kl, vl = up(qh2, wl.dtype), up(kh2, wl.dtype), up(vh2, wl.dtype)
+            sk = torch.from_numpy(sh2).to(dev)
+            ol = torch.empty(ql.shape, dtype=torch.bfloat16, device=dev)
+            ll = torch.empty(ql.shape[:3], dtype=torch.float32, device=dev)
+            fn = (lambda ql=ql, kl=kl, vl=vl, sk=sk, ol=ol, ll=ll, wl=wl:
+                  A.attn_fwd(ql, kl, vl, sk, ol, ll, window=wl.window, scale=wl.scale,
+                             stream=stream))
+            t = time_launches(torch, stream, fn, args.leg_launches)
+            traffic = stored_traffic("fwd_bf16_kernel<128,false,false,false>:" + wl.name)
+            legs[name] = {"workload": describe(wl),
+                          "roofline": prefill_roofline(wl, t, traffic)}
+            leg_inputs[name] = (wl, ql, kl, vl, sk)
+
+    # Extras on the sliding-window prefill's inputs (B1 L8192): backward,
+    # split-count policies, serving layouts, the max-logit output.
+    extras = {}
+    if not args.step_only and "swa_prefill" in leg_inputs:
+        wl, ql, kl, vl, sk = leg_inputs["swa_prefill"]
+        say("bench: extras")
+        extras["split_policy"] = measure_split_policies(
+            A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd, seqlens)
+        extras["serving"] = measure_serving(
+            A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
+            t_dec.mean() + t_cmb.mean(), wl)
+        extras["backward"] = measure_backward(A, torch, dev, stream, ql, kl, vl, sk, wl)
+        ol = torch.empty(ql.shape, dtype=torch.bfloat16, device=dev)
+        ll = torch.empty(ql.shape[:3], dtype=torch.float32, device=dev)
+        ml_row = torch.empty(ll.shape, dtype=torch.float32, device=dev)
+        ml_head = torch.empty(ll.shape[:2], dtype=torch.float32, device=dev)
+        t_ml = time_launches(torch, stream, lambda: A.attn_fwd_max_logit(
+            ql, kl, vl, sk, ol, ll, ml_row, ml_head, window=wl.window, scale=wl.scale,
+            stream=stream), 50)
+        t_ref = legs["swa_prefill"]["roofline"]["ms_per_launch"] * 1e-3
+        extras["max_logit"] = {
+            "entry": "attn_fwd_max_logit (row [B,Hq,Lq] and head [B,Hq] maxima), swa_prefill",
+            "ms_per_launch": round(t_ml.mean() * 1e3, 4),
+            "TFLOP/s": round(wl.flops() / t_ml.mean() / 1e12, 2),
+            "time_vs_attn_fwd": round(t_ml.mean() / t_ref, 4),
+        }
 
     flops = wp.flops()
     tflops = flops / t_fwd.mean() / 1e12
@@ -569,6 +673,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm": {"gpu_ms": round(prewarm_s * 1e3, 1), "steps": prewarm_steps},
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -576,26 +681,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{wp.name} B{wp.B} Hq{wp.Hq} Hkv{wp.Hkv} L{wp.L} D{wp.D} window{wp.window} "
-                        f"+ {wd.name} B{wd.B} Hq{wd.Hq} Hkv{wd.Hkv} D{wd.D} Lk<={wd.Lk_max}",
+            "workload": f"{describe(wp)} + {wd.name} B{wd.B} Hq{wd.Hq} Hkv{wd.Hkv} D{wd.D} "
+                        f"Lk<={wd.Lk_max}",
             "prefill_flops": flops,
             "decode_bytes": dbytes,
             "decode_sum_Lk": int(np.asarray(seqlens, np.int64).sum()),
             "decode_keys_per_split": args.keys_per_split or wd.keys_per_split,
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "kernel": "fwd_bf16_kernel<128,false,false,false>",
-            "ms_per_launch": round(t_fwd.mean() * 1e3, 4),
-            "ms_median": round(float(np.median(t_fwd)) * 1e3, 4),
-            "ms_min": round(float(t_fwd.min()) * 1e3, 4),
-            "host_us_per_call": round(host_fwd, 1),
-        },
+        "roofline": prefill_roofline(wp, t_fwd, traffic, host_fwd),
         "decode": {
             "GB/s": round(dec_gbps, 1),
             "frac_hbm": round(dec_gbps / PEAK_HBM_GBPS, 4),
@@ -620,18 +713,14 @@ def main():
             "host_us_per_call": round(host_dec, 1),
         },
     }
-    if not args.step_only:
-        res["backward"] = bwd
-        res["split_policy"] = split_policy
-        res["serving"] = serving
-        res["max_logit"] = {
-            "entry": "attn_fwd_max_logit (row [B,Hq,Lq] and head [B,Hq] maxima)",
-            "ms_per_launch": round(t_ml.mean() * 1e3, 4),
-            "TFLOP/s": round(flops / t_ml.mean() / 1e12, 2),
-            "time_vs_attn_fwd": round(t_ml.mean() / t_fwd.mean(), 4),
-        }
+    if legs:
+        res["prefill_legs"] = legs
+    res.update(extras)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wp, qh, kh, vh, sh)
+        say("bench: oracle baselines")
+        res["cpu_baseline"] = cpu_baseline(wp, *host[wp.name])
+        for name, leg in legs.items():
+            leg["cpu_baseline"] = cpu_baseline(W.WORKLOADS[name], *host[name])
         res["cpu_baseline_decode"] = cpu_baseline_decode(wd, dq, kv_host, seqlens, nsplits, dsinks)
     print(json.dumps(res), flush=True)
 
