@@ -132,10 +132,12 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
 
     Rows: the decode workload of the step, and two synthetic mixes drawn on
     the device (4 sequences of 32768 keys; 256 sequences of 128..2048 keys).
-    'auto' times attn_decode_plan + decode + combine; fixed rules time
-    decode + combine with counts planned beforehand.
+    Every rule times decode + combine with the counts planned beforehand (a
+    caller plans once per step and can reuse the plan while its lengths
+    stand); 'auto+plan' also times the planning launch (attn_decode_plan)
+    inside every call.  auto_vs_best_fixed = auto / the fastest fixed rule.
     """
-    def timed(q_, k_, v_, sl_, Lk_max, policy, param, nbytes):
+    def timed(q_, k_, v_, sl_, Lk_max, policy, param, nbytes, with_plan=False):
         B, Hq = q_.shape[0], q_.shape[1]
         ns = torch.empty(B, dtype=torch.int32, device=dev)
         plan = lambda: A.attn_decode_plan(sl_, ns, Hq=Hq, Hkv=k_.shape[1], Lk_max=Lk_max,
@@ -149,7 +151,7 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
             lse_ = torch.empty((B,) + tuple(dlse.shape[1:]), dtype=dlse.dtype, device=dev)
 
         def once():
-            if policy == "auto":
+            if with_plan:
                 plan()
             A.attn_decode_splitkv(q_, k_, v_, sl_, ns, o_, l_, window=0, scale=wd.scale,
                                   stream=stream)
@@ -158,7 +160,8 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
         with torch.cuda.stream(stream):
             plan()
         ms = warm_then_time(torch, stream, once, reps) * 1e3
-        return {"policy": f"{policy}({param})" if policy != "auto" else "auto",
+        label = f"{policy}({param})" if policy != "auto" else ("auto+plan" if with_plan else "auto")
+        return {"policy": label,
                 "us": round(ms * 1e3, 1), "GB/s": round(nbytes / ms / 1e6, 1),
                 "total_splits": int(ns.sum().item())}
 
@@ -178,7 +181,11 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
         nbytes = decode_bytes(lens, Hq, Hkv, D, 0)
         res = [timed(q_, k_, v_, sl_, Lk_max, pol, par, nbytes)
                for pol, par in (("auto", 0), ("keys", 1024), ("keys", 512), ("count", 1))]
-        rows.append({"workload": name, "results": res})
+        res.append(timed(q_, k_, v_, sl_, Lk_max, "auto", 0, nbytes, with_plan=True))
+        best_fixed = min(r["us"] for r in res if not r["policy"].startswith("auto"))
+        rows.append({"workload": name, "results": res,
+                     "auto_vs_best_fixed": round(res[0]["us"] / best_fixed, 4),
+                     "auto+plan_vs_best_fixed": round(res[-1]["us"] / best_fixed, 4)})
     return rows
 
 

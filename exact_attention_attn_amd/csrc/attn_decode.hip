@@ -573,15 +573,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombArgs a) {
 // Split-count planning (attn_decode_plan).  One work-group; for the auto
 // policy every thread accumulates, over its sequences, the item count and the
 // largest split of each candidate chunk target; threads 0..10 then price one
-// candidate each and thread 0 takes the first of least estimated cost (rule
-// stated in include/attn.h).  Item counts fit in 32 bits (the API bounds
+// candidate each, as the items of the most loaded compute unit times the
+// largest split plus a per-item cost, and thread 0 takes the first of least
+// estimated cost (rule stated in include/attn.h).  Item counts fit in 32 bits (the API bounds
 // B*Hq*max_splits below 2^31); dividing by the candidate targets, which are
 // compile-time constants, costs a multiply.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 256;
 constexpr int kPlanCands = 11;
 constexpr int kPlanChunks[kPlanCands] = {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192};
-constexpr long long kPlanItemCost = 80;  // per-item overhead, in key rows
+constexpr long long kPlanItemCost = 400;  // per-item cost beyond its keys, in key rows
 
 struct PlanArgs {
   const int32_t* seqlens;
@@ -600,7 +601,6 @@ __device__ __forceinline__ int splits_for(int n, int target, int max_splits) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_items[kPlanCands][kPlanThreads / 64];
   __shared__ int s_z[kPlanCands][kPlanThreads / 64];
-  __shared__ long long s_T[kPlanThreads / 64];
   __shared__ long long s_cost[kPlanCands];
   __shared__ int s_target;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -608,10 +608,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int items[kPlanCands], z[kPlanCands];
 #pragma unroll
     for (int i = 0; i < kPlanCands; ++i) { items[i] = 0; z[i] = 0; }
-    long long T = 0;
     for (int b = tid; b < a.B; b += kPlanThreads) {
       const int n = visible_n(a.seqlens[b], a.Lk_max, a.window);
-      T += n;
       if (n == 0) continue;
 #pragma unroll
       for (int i = 0; i < kPlanCands; ++i) {
@@ -623,7 +621,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      T += __shfl_xor(T, o);
 #pragma unroll
       for (int i = 0; i < kPlanCands; ++i) {
         items[i] += __shfl_xor(items[i], o);
@@ -631,26 +628,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
     }
     if (lane == 0) {
-      s_T[wave] = T;
 #pragma unroll
       for (int i = 0; i < kPlanCands; ++i) { s_items[i][wave] = items[i]; s_z[i][wave] = z[i]; }
     }
     __syncthreads();
     if (tid < kPlanCands) {
-      long long tot = 0;
       int it = 0, zz = 0;
 #pragma unroll
       for (int w = 0; w < kPlanThreads / 64; ++w) {
-        tot += s_T[w];
         it += s_items[tid][w];
         zz = max(zz, s_z[tid][w]);
       }
-      tot *= a.hq;
       it *= a.hq;
       const unsigned S = (unsigned)a.slots;  // >= 1
       const long long per = ((unsigned)it + S - 1u) / S;  // < 2^32: it < 2^31, S <= 2^31
-      const long long ts = (tot + S - 1) / S;
-      s_cost[tid] = min(per * zz, ts + zz) + kPlanItemCost * per;
+      s_cost[tid] = per * (zz + kPlanItemCost);
     }
     __syncthreads();
     if (tid == 0) {

@@ -219,16 +219,17 @@ int attn_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_
  *   ATTN_SPLITS_AUTO   num_splits[b] = ceil(n_b / c) for the chunk target c in
  *                      {256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096,
  *                      6144, 8192} that minimises
- *                        min(per * Z, ceil(T / S) + Z) + 80 * per,
- *                      per = ceil(I / S), with, for target c: I the decode's
- *                      work items (valid splits x Hkv x ceil((Hq/Hkv)/32)),
- *                      Z the largest split in keys, T = sum_b n_b x Hkv x
- *                      ceil((Hq/Hkv)/32) and S the units the items are
- *                      spread over (param, or the compute units when
- *                      param = 0).  The first (smallest) such c wins.  The
- *                      estimate is the keys of the most loaded unit plus a
- *                      per-item overhead of 80 key rows, both fitted to
- *                      measurements on MI355X.
+ *                        ceil(I / S) * (Z + 400),
+ *                      with, for target c: I the decode's work items (valid
+ *                      splits x Hkv x ceil((Hq/Hkv)/32)), Z the largest split
+ *                      in keys and S the units the items are spread over
+ *                      (param, or the compute units when param = 0).  The
+ *                      first (smallest) such c wins.  The estimate is the
+ *                      items of the most loaded unit, each priced as the
+ *                      largest split plus a per-item cost of 400 key rows;
+ *                      the form and the constant were fitted to decode +
+ *                      combine times of every target on eight batch/length
+ *                      mixes on MI355X (choice within 1% of the best).
  * seqlens_k [B] int32 (device); num_splits [B] int32 (device, written).
  * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE (sizes as in attn_decode_splitkv),
  * ATTN_ERR_UNSUPPORTED (unknown policy), ATTN_ERR_VALUE (param < 1 for

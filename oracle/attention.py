@@ -347,7 +347,7 @@ def split_ranges(Lk: int, num_splits: int, window: int) -> list[tuple[int, int]]
 # include/attn.h, and restated here step by step.
 PLAN_COUNT, PLAN_KEYS, PLAN_AUTO = "count", "keys", "auto"
 PLAN_CHUNKS = (256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
-PLAN_ITEM_COST = 80  # per-item overhead of the decode, in key rows
+PLAN_ITEM_COST = 400  # per-item cost of the decode beyond its keys, in key rows
 
 
 def visible_keys(seqlen: int, Lk_max: int, window: int) -> int:
@@ -363,13 +363,13 @@ def plan_splits(seqlens, Hq: int, Hkv: int, Lk_max: int, window: int, max_splits
 
     count: every sequence gets param splits; keys: ceil(n/param) splits for n
     visible keys; auto: the chunk target c from PLAN_CHUNKS that minimises
-        min(per * Z, ceil(T / S) + Z) + PLAN_ITEM_COST * per,
-    per = ceil(I / S), where for target c every sequence takes ceil(n/c)
-    splits, I counts the decode's work items (valid splits x KV heads x
-    query-column groups of 32), Z is the largest split in keys, T the visible
-    key rows times KV heads and groups, and S the units the items are spread
-    over (slots).  The first such c wins.  Splits are clamped to
-    [1, max_splits] in every policy.
+        ceil(I / S) * (Z + PLAN_ITEM_COST),
+    where for target c every sequence takes ceil(n/c) splits, I counts the
+    decode's work items (valid splits x KV heads x query-column groups of
+    32), Z is the largest split in keys and S the units the items are spread
+    over (slots): the items of the most loaded unit, each priced as the
+    largest split plus a fixed per-item cost.  The first such c wins.
+    Splits are clamped to [1, max_splits] in every policy.
     """
     ns_of = lambda n, c: min(max(-(-n // c), 1), max_splits)
     ns_clamp = lambda x: min(max(int(x), 1), max_splits)
@@ -382,7 +382,6 @@ def plan_splits(seqlens, Hq: int, Hkv: int, Lk_max: int, window: int, max_splits
         raise ValueError(policy)
     G = Hq // Hkv
     hq = Hkv * (-(-G // 32))
-    T = hq * sum(lens)
     best = None
     for c in PLAN_CHUNKS:
         items, z = 0, 0
@@ -394,7 +393,7 @@ def plan_splits(seqlens, Hq: int, Hkv: int, Lk_max: int, window: int, max_splits
             z = max(z, max(e - a for a, e in parts))
         items *= hq
         per = -(-items // slots)
-        cost = min(per * z, -(-T // slots) + z) + PLAN_ITEM_COST * per
+        cost = per * (z + PLAN_ITEM_COST)
         if best is None or cost < best[0]:
             best = (cost, c)
     return [ns_of(n, best[1]) for n in lens]

@@ -266,7 +266,7 @@ def err_max_logit_gqa(seed=0, Hq=8, Hkv=2, L=30, D=8, window=5):
 # The planning rule as include/attn.h states it, retyped here on purpose so
 # that a changed constant in the oracle shows up.
 RULE_CHUNKS = (256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192)
-RULE_ITEM_COST = 80
+RULE_ITEM_COST = 400
 
 
 def brute_plan_auto(seqlens, Hq, Hkv, Lk_max, window, max_splits, slots):
@@ -278,7 +278,6 @@ def brute_plan_auto(seqlens, Hq, Hkv, Lk_max, window, max_splits, slots):
         Lk = min(max(int(x), 0), Lk_max)
         lo = max(0, Lk - window) if window > 0 else 0
         lens.append(Lk - lo)
-    total = hq * sum(lens)
     best_cost, best_c = None, None
     for c in RULE_CHUNKS:
         items, zmax = 0, 0
@@ -295,7 +294,7 @@ def brute_plan_auto(seqlens, Hq, Hkv, Lk_max, window, max_splits, slots):
                 start += chunk
         items *= hq
         per = math.ceil(items / slots)
-        cost = min(per * zmax, math.ceil(total / slots) + zmax) + RULE_ITEM_COST * per
+        cost = per * (zmax + RULE_ITEM_COST)
         if best_cost is None or cost < best_cost:
             best_cost, best_c = cost, c
     return [min(max(math.ceil(n / best_c), 1), max_splits) for n in lens]
