@@ -64,17 +64,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel: str):
-    """HBM bytes per launch measured with rocprofv3 counters for the current sources, or None."""
+def stored_profile(kernel: str) -> dict:
+    """What rocprofv3 counters measured for this kernel and workload with the current
+    sources (HBM bytes per launch, sustained clock), or {} when they no longer apply."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         data = json.load(f)
     ent = data.get(kernel)
     if not ent or ent.get("source_hash") != kernel_source_hash():
-        return None
-    return ent.get("bytes_per_launch")
+        return {}
+    return ent
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current sources, or None."""
+    return stored_profile(kernel).get("bytes_per_launch")
 
 
 def decode_bytes(seqlens, Hq, Hkv, D, window) -> int:
@@ -440,8 +446,14 @@ def time_launches(torch, stream, fn, n, prewarm_s=0.05):
 
 
 def prefill_roofline(wp, t, traffic, host_us=None):
-    """Roofline object of one prefill workload from per-launch seconds t."""
+    """Roofline object of one prefill workload from per-launch seconds t.
+
+    frac is against the published bf16 peak (2.5 PF at 2.4 GHz).  When the
+    counter profile of these sources is stored, the sustained clock it measured
+    under this kernel (active cycles over dispatch time) is reported beside it,
+    with the fraction of the peak at that clock (context, not the bar)."""
     tflops = wp.flops() / t.mean() / 1e12
+    clock = stored_profile("fwd_bf16_kernel<128,false,false,false>:" + wp.name).get("clock_ghz")
     r = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
          "kernel": "fwd_bf16_kernel<128,false,false,false>",
@@ -450,7 +462,10 @@ def prefill_roofline(wp, t, traffic, host_us=None):
          "ms_median": round(float(np.median(t)) * 1e3, 4),
          "ms_min": round(float(t.min()) * 1e3, 4),
          "frac_median": round(wp.flops() / float(np.median(t)) / 1e12 / PEAK_BF16_TFLOPS, 4),
-         "launches": int(len(t))}
+         "launches": int(len(t)),
+         "sustained_clock_ghz": clock,
+         "frac_at_sustained_clock": (round(tflops / (PEAK_BF16_TFLOPS * clock / 2.4), 4)
+                                     if clock else None)}
     if host_us is not None:
         r["host_us_per_call"] = round(host_us, 1)
     return r
