@@ -196,15 +196,16 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
 
 
 def measure_backward(A, torch, dev, stream, q, k, v, s, wp, reps=10):
-    """attn_bwd on the step's prefill: dQ, dK, dV and dsink for a seeded dO.
+    """attn_bwd on the step's prefill: dQ, dK, dV and dsink for a seeded dO,
+    given the bf16 O that the forward writes in the step.
 
     Algorithmic work is the five products of the backward (S, dP, dV, dK, dQ:
-    10*D flops per unmasked pair, 2.5x the forward); the dQ phase recomputes
-    S and dP, so the kernels execute 14*D per pair.
+    10*D flops per unmasked pair, 2.5x the forward); the two phases both
+    compute S and dP, so the kernels execute 14*D per pair.
     """
     g = torch.Generator(device=dev)
     g.manual_seed(5)
-    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
     dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
@@ -218,11 +219,11 @@ def measure_backward(A, torch, dev, stream, q, k, v, s, wp, reps=10):
                              scale=wp.scale, stream=stream)
     t = warm_then_time(torch, stream, run, reps)
     pairs = wp.flops() // (4 * wp.D)
-    return {"entry": "attn_bwd (dQ, dK, dV, dsink)", "ms": round(t * 1e3, 4),
+    return {"entry": "attn_bwd (dQ, dK, dV, dsink), bf16 O", "ms": round(t * 1e3, 4),
             "TFLOP/s": round(10 * wp.D * pairs / t / 1e12, 2),
             "executed_TFLOP/s": round(14 * wp.D * pairs / t / 1e12, 2),
-            "note": "TFLOP/s counts the 5 backward products (10*D per pair); the dQ phase "
-                    "recomputes S and dP (14*D per pair executed)"}
+            "note": "TFLOP/s counts the 5 backward products (10*D per pair); both phases "
+                    "compute S and dP (14*D per pair executed)"}
 
 
 def combine_bytes(seqlens, nsplits, Hq, D, window, max_splits=64) -> int:

@@ -5,21 +5,23 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q,  dsink_h = -sum_{b,i} Psink_i D_i
 // (the sink joins the normaliser and has no value vector, so it enters dS
-// only through D).  Four kernels, all deterministic (no atomics):
-//   bwd_delta_kernel  D_i = <dO_i, O_i> from the forward's O, for dS;
+// only through D).  Three kernels in stream order, all deterministic (no
+// atomics):
 //   bwd_dq_kernel     rows fixed, K/V tiles streamed (the forward's layout):
-//                     S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T; it
-//                     also sums D_i = sum_j P_ij dP_ij with fp32 P, which is
-//                     <dO_i, O_i> for the exact O -- so dsink does not inherit
-//                     the bf16 rounding of P inside the forward's O (the dsink
+//                     D_i = <dO_i, O_i> from the forward's O in its prologue,
+//                     then S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
+//                     it also sums D_i = sum_j P_ij dP_ij with fp32 P, which
+//                     is <dO_i, O_i> for the exact O, and leaves that in the
+//                     workspace -- so dK/dV and dsink do not inherit the bf16
+//                     rounding of P inside the forward's O (the dsink
 //                     precision issue #2969 of the flash-attention profile);
-//   bwd_dsink_kernel  one work-group per query head, fixed summation order;
-//   bwd_dkdv_kernel   keys fixed (16 per wave, 16x16x32 MFMAs), the G query
+//   bwd_dkdv_kernel   keys fixed (32 per wave, 32x32x16 MFMAs), the G query
 //                     heads' Q/dO tiles streamed: S = Q K^T, dP = dO V^T,
-//                     dV^T += dO^T P, dK^T += Q^T dS.
-// The two-phase split (dK/dV, then dQ) is the flash-attention profile's
-// backward call flow; P and dS are rounded to bf16 for the MFMAs and every
-// sum is fp32.
+//                     dV^T += dO^T P, dK^T += Q^T dS;
+//   bwd_dsink_kernel  one work-group per query head, fixed summation order.
+// The two-phase split (one pass with rows fixed, one with keys fixed) is the
+// flash-attention profile's backward call flow; P and dS are rounded to bf16
+// for the MFMAs and every sum is fp32.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 #include "attn_tiles.hpp"
@@ -47,58 +49,6 @@ struct BwdArgs {
   float c;      // scale * log2(e)
   float scale;
 };
-
-// ---------------------------------------------------------------------------
-// D_i = <dO_i, O_i>: 16 lanes per row, D/16 elements each, fixed reduction.
-// A 16-lane group takes kDeltaRows rows per pass and issues all their loads
-// (non-temporal: every byte is read once) before the first product.
-// ---------------------------------------------------------------------------
-constexpr int kDeltaRows = 4;
-
-template <int D, bool O_F32>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  constexpr int E = D / 16;  // elements per lane: 8 (D = 128) or 4 (D = 64)
-  constexpr int R = kDeltaRows;
-  using OT = typename std::conditional<O_F32, float, uint16_t>::type;
-  using GV = typename std::conditional<E == 8, u32x4, u32x2>::type;  // E bf16
-  constexpr int ON = E * (int)sizeof(OT) / 16 > 0 ? E * (int)sizeof(OT) / 16 : 1;
-  using OV = typename std::conditional<E * sizeof(OT) >= 16, u32x4, u32x2>::type;
-  const long long rows = (long long)a.B * a.Hq * a.Lq;
-  const int sub = threadIdx.x & 15;
-  const long long groups = (long long)gridDim.x * 16;
-  for (long long row0 = ((long long)blockIdx.x * 16 + (threadIdx.x >> 4)) * R; row0 < rows;
-       row0 += groups * R) {
-    GV g[R];
-    OV o[R][ON];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const long long row = min(row0 + r, rows - 1);  // in bounds; the extra rows are not stored
-      g[r] = __builtin_nontemporal_load((const GV*)(a.dout + row * D + sub * E));
-#pragma unroll
-      for (int j = 0; j < ON; ++j)
-        o[r][j] = __builtin_nontemporal_load((const OV*)((const OT*)a.o + row * D + sub * E) + j);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint16_t* gs = (const uint16_t*)&g[r];
-      const OT* os = (const OT*)&o[r][0];
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float go = __builtin_bit_cast(float, (uint32_t)gs[e] << 16);
-        float ov;
-        if constexpr (O_F32)
-          ov = os[e];
-        else
-          ov = __builtin_bit_cast(float, (uint32_t)os[e] << 16);
-        acc = __builtin_fmaf(go, ov, acc);
-      }
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-      if (sub == 0 && row0 + r < rows) a.delta[row0 + r] = acc;
-    }
-  }
-}
 
 // dsink[h] = -sum over (b, i) of exp(sink_h - LSE) * D, one work-group of
 // 1024 threads per head: each thread sums a fixed strided subset (kSinkUnroll
@@ -204,7 +154,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* ks_, const lds_char* vs_
   }
 }
 
-template <int D>
+template <int D, bool O_F32>
 __global__ __launch_bounds__(kBfThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   lds_char* K0 = BfSmem<D>::template k<0>();
   lds_char* K1 = BfSmem<D>::template k<1>();
@@ -257,7 +207,41 @@ __global__ __launch_bounds__(kBfThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   // An invalid row gets lse2 = +inf: its P is 0 and it adds nothing.
   const float lse2 = row_valid ? a.lse[q_row0 + my_row] * kLog2e : __builtin_huge_valf();
-  const float dl = row_valid ? a.delta[q_row0 + my_row] : 0.0f;
+  // D_i = <dO_i, O_i> for dS in this kernel: the lane holds dO at d = 16 ks +
+  // 8 half .. +8 of its row (df) and reads O at the same places; the halves'
+  // sums meet in pair_sum.
+  float dl = 0.0f;
+  if (row_valid) {
+    const size_t orow = (q_row0 + my_row) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int d0 = ks * 16 + half * 8;
+      float ov[8];
+      if constexpr (O_F32) {
+        const f32x4 o0 = *(const f32x4*)((const float*)a.o + orow + d0);
+        const f32x4 o1 = *(const f32x4*)((const float*)a.o + orow + d0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ov[e] = o0[e];
+          ov[e + 4] = o1[e];
+        }
+      } else {
+        const u32x4 w = *(const u32x4*)((const uint16_t*)a.o + orow + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ov[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+          ov[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
+        }
+      }
+      const u32x4 g = __builtin_bit_cast(u32x4, df[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dl = __builtin_fmaf(__builtin_bit_cast(float, g[e] << 16), ov[2 * e], dl);
+        dl = __builtin_fmaf(__builtin_bit_cast(float, g[e] & 0xffff0000u), ov[2 * e + 1], dl);
+      }
+    }
+  }
+  dl = pair_sum(dl);
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
@@ -295,8 +279,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // D_i again, now as sum_j P_ij dP_ij with fp32 P: equal to <dO_i, O_i> for
   // the exact O, free of the bf16 rounding of P that the forward's O carries.
-  // It replaces the workspace value (the dK/dV kernel, earlier on the stream,
-  // is done with it) for dsink.
+  // The dK/dV kernel, next on the stream, and dsink take it from the
+  // workspace.
   const float d_exact = pair_sum(dsum);
   if (row_valid && half == 0) a.delta[q_row0 + my_row] = d_exact;
   // dQ (fp32, 16 KB per wave) through a whole K/V array per wave, once every
@@ -307,21 +291,30 @@ __global__ __launch_bounds__(kBfThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: a work-group owns 64 keys of one (batch, KV head), 16 per wave, and
+// dK, dV: a work-group owns 128 keys of one (batch, KV head), 32 per wave, and
 // streams 32-row tiles of Q and dO (plus their LSE and D) of every query head
 // of the group whose rows can see those keys, through a two-stage LDS ring.
-//
-// v_mfma_f32_16x16x32_bf16 throughout.  S = Q K^T puts the keys in the lane
-// (column) dimension: lane l of lane group g = l/16 holds key l%16 and, over
-// its 2 row blocks x 4 registers, rows 8g .. 8g+7 of the tile -- because the
-// A-operand rows of block b are read in the order m -> 8(m/4) + 4b + m%4.
-// That is exactly the k-order the B operand (P or dS, rows x keys) of
-// dV^T += dO^T P and dK^T += Q^T dS needs, so P and dS go to the MFMAs
-// straight from their registers; dO^T and Q^T come from transposed LDS reads.
+// v_mfma_f32_32x32x16_bf16 throughout; per step, a wave computes for its 32
+// keys x the tile's 32 rows:
+//   S  = Q K^T    A: Q rows from LDS, read in key_perm order; B: K^T in VGPRs
+//   dP = dO V^T   A: dO rows likewise; B: V^T from the work-group's V block
+//   P = exp2(c S - LSE log2e), dS = P (dP - D)   (lane: one key, 16 rows)
+//   dV^T += dO^T P, dK^T += Q^T dS   A: transposed LDS reads; B: P and dS
+//                 straight from the accumulator registers (key_perm makes their
+//                 row order the k order of these B operands)
+// The S accumulator starts at -LSE/scale and the dP accumulator at -D, so the
+// MFMAs deliver c S - LSE log2e (after one multiply by c) and dP - D directly.
+// Each K^T/V^T operand byte read feeds a 32x32x16 MFMA: half the LDS bytes per
+// flop of 16-key blocks on 16x16x32 MFMAs.  V sits in LDS (not in VGPRs) so
+// that K^T, the dK^T/dV^T accumulators and two 32x32 tiles fit in the 256
+// registers of two waves per SIMD; its rows are stored in key_perm order
+// within each wave's 32 keys, so a V^T operand read has the address of the
+// Q row read of the same k-step, and one set of address registers serves Q,
+// dO and V.
 // ---------------------------------------------------------------------------
-constexpr int kKvKeys = 64;  // keys per work-group
-constexpr int kKvWaveKeys = 16;
-constexpr int kKvRows = 32;  // query rows per streamed tile
+constexpr int kKvWaveKeys = 32;
+constexpr int kKvKeys = kKvWaveKeys * kBfWaves;  // keys per work-group
+constexpr int kKvRows = 32;                      // query rows per streamed tile
 
 template <int D>
 struct KvSmem {
@@ -337,8 +330,12 @@ struct KvSmem {
     return (lds_char*)buf;
   }
   template <int I>
-  static __device__ __forceinline__ lds_char* s() {  // 64 LSE values, then 64 D values
+  static __device__ __forceinline__ lds_char* s() {  // 64 LSE slots, then 64 D slots
     __shared__ __attribute__((aligned(256))) char buf[512];
+    return (lds_char*)buf;
+  }
+  static __device__ __forceinline__ lds_char* v() {  // the work-group's V rows
+    __shared__ __attribute__((aligned(1024))) char buf[kKvKeys * D * 2];
     return (lds_char*)buf;
   }
 };
@@ -385,59 +382,91 @@ struct RowTileCopy {
   }
 };
 
+// The work-group's V rows [k0, k0 + 128) into the V block: LDS row R (BfTile
+// swizzle) holds key k0 + (R & ~31) + key_perm(R & 31); keys past Lk arrive as
+// zeros.  32 KB (D = 128) in 1 KB pieces, each wave a quarter.
 template <int D>
-__device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs, const lds_char* ss,
-                                          const int (&qa)[2][D / 32], const int (&ta)[2][D / 16],
-                                          const bf16x8 (&kf)[D / 32], const bf16x8 (&vf)[D / 32],
-                                          f32x4 (&dk)[D / 16], f32x4 (&dv)[D / 16], int kind,
-                                          int row_base, int key, int p_off, int Lq, int Lk,
-                                          int window, int g16, float c) {
-  constexpr int KS = D / 32;
-  constexpr int NDB = D / 16;
-  f32x4 s[2] = {(f32x4){}, (f32x4){}}, dp[2] = {(f32x4){}, (f32x4){}};
+__device__ __forceinline__ void copy_v_block(const uint16_t* vh, int k0, int Lk, lds_char* dst,
+                                             int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using L = BfLayout<D>;
+  constexpr int kPieces = kKvKeys * L::kRow / 1024;
+  const int bytes = min(kKvKeys, Lk - k0) * L::kRow;
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)vh + (size_t)k0 * L::kRow), 0, bytes, kRawBufferWord3);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = mfma_16x16x32(as_bf16x8(lds_read16(qs, qa[b][ks])), kf[ks], s[b]);
-      dp[b] = mfma_16x16x32(as_bf16x8(lds_read16(gs, qa[b][ks])), vf[ks], dp[b]);
-    }
-  // LSE and D of the lane group's rows 8g16 .. 8g16+7
-  const f32x4 l0 = *(const __attribute__((address_space(3))) f32x4*)(ss + g16 * 32);
-  const f32x4 l1 = *(const __attribute__((address_space(3))) f32x4*)(ss + g16 * 32 + 16);
-  const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(ss + 256 + g16 * 32);
-  const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(ss + 256 + g16 * 32 + 16);
-  float pv[8], dsv[8];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float lse = b ? l1[r] : l0[r];
-      const float dlt = b ? d1[r] : d0[r];
-      float p = exp2_fast(__builtin_fmaf(s[b][r], c, -lse * kLog2e));
-      if (kind == 2) {
-        const int i = row_base + 8 * g16 + 4 * b + r;  // query row
-        const int pos = i + p_off;
-        const bool vis = i < Lq && key < Lk && key <= pos && (window <= 0 || key > pos - window);
-        p = vis ? p : 0.0f;
-      }
-      pv[4 * b + r] = p;
-      dsv[4 * b + r] = p * (dp[b][r] - dlt);
-    }
-  const bf16x8 pp = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-  const bf16x8 pd = pack_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const bf16x8 gt = join_tr(lds_read_tr16(gs, ta[0][db]), lds_read_tr16(gs, ta[1][db]));
-    dv[db] = mfma_16x16x32(gt, pp, dv[db]);
-    const bf16x8 qt = join_tr(lds_read_tr16(qs, ta[0][db]), lds_read_tr16(qs, ta[1][db]));
-    dk[db] = mfma_16x16x32(qt, pd, dk[db]);
+  for (int j = 0; j < kPieces / kBfWaves; ++j) {
+    const int pc = wave + j * kBfWaves;
+    const int R = pc * L::kRowsPerPiece + lane / L::kChunks;
+    const int g = (R & ~31) | key_perm(R & 31);
+    const int c = (lane % L::kChunks) ^ BfTile<D>::swz(R);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, dst + pc * 1024, 16, (uint32_t)(g * L::kRow + c * 16),
+                                             0, 0, 0);
   }
+#endif
 }
 
-// At most two waves per SIMD: the compiler then schedules with up to 256
-// registers (176 used) instead of fitting three waves in 160, and the backward
-// measured 3% faster on both the sliding-window and causal shapes.
+template <int D>
+__device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs, const lds_char* ss,
+                                          const lds_char* vw, const int (&qa)[D / 16],
+                                          const int (&ta)[2][D / 32], const bf16x8 (&kf)[D / 16],
+                                          f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int kind,
+                                          int vis_lo, unsigned vis_span, int half, float c,
+                                          float inv_scale) {
+  constexpr int KS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int kRow = D * 2;
+  // register v of the lane holds row key_of_reg(v, half): rows 8h .. 8h+7
+  // (v < 8) and 16+8h .. 16+8h+7 (v >= 8), four per 16 B read
+  f32x16 s, dp;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = (j >> 1) * 16 + half * 8 + (j & 1) * 4;
+    const f32x4 l = *(const __attribute__((address_space(3))) f32x4*)(ss + r * 4);
+    const f32x4 d = *(const __attribute__((address_space(3))) f32x4*)(ss + 256 + r * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[4 * j + e] = -l[e] * inv_scale;
+      dp[4 * j + e] = -d[e];
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    s = mfma_32x32x16(as_bf16x8(lds_read16(qs, qa[ks])), kf[ks], s);
+    dp = mfma_32x32x16(as_bf16x8(lds_read16(gs, qa[ks])), as_bf16x8(lds_read16(vw, qa[ks])), dp);
+  }
+  // register v sits at row offset key_of_reg(v, 0) from the lane's first row
+  // (row_base + 8 half); it is visible iff that offset lies in
+  // [vis_lo, vis_lo + vis_span]
+  float pv[16], dsv[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float p = exp2_fast(s[v] * c);
+    if (kind == 2) p = ((unsigned)(key_of_reg(v, 0) - vis_lo) <= vis_span) ? p : 0.0f;
+    pv[v] = p;
+    dsv[v] = p * dp[v];
+  }
+  bf16x8 pp[2], pd[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const float* x = pv + 8 * k2;
+    const float* y = dsv + 8 * k2;
+    pp[k2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    pd[k2] = pack_bf16x8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int rows = k2 * 16 * kRow;
+      const bf16x8 gt = join_tr(lds_read_tr16(gs, ta[0][db] + rows), lds_read_tr16(gs, ta[1][db] + rows));
+      dv[db] = mfma_32x32x16(gt, pp[k2], dv[db]);
+      const bf16x8 qt = join_tr(lds_read_tr16(qs, ta[0][db] + rows), lds_read_tr16(qs, ta[1][db] + rows));
+      dk[db] = mfma_32x32x16(qt, pd[k2], dk[db]);
+    }
+}
+
+// At most two waves per SIMD (the registers allow no more).
 template <int D>
 __global__ __launch_bounds__(kBfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
@@ -447,62 +476,74 @@ void bwd_dkdv_kernel(BwdArgs a) {
   lds_char* G1 = KvSmem<D>::template g<1>();
   lds_char* S0 = KvSmem<D>::template s<0>();
   lds_char* S1 = KvSmem<D>::template s<1>();
+  lds_char* VB = KvSmem<D>::v();
 
+  // Key block kb of (batch, KV head) hh.  Each XCD (work-groups are dealt
+  // round-robin over 8) runs whole (batch, KV head) groups, so the Q/dO tiles
+  // they share stay in its L2, and takes its key blocks in ascending order:
+  // under a causal mask the earliest keys see the most rows, so the longest
+  // work-groups start first.
   const int nkb = (a.Lk + kKvKeys - 1) / kKvKeys;
-  const int id = xcd_remap(blockIdx.x, nkb * a.Hkv * a.B);
-  const int kb = id % nkb;
-  const int kvh = (id / nkb) % a.Hkv;
-  const int b = id / (nkb * a.Hkv);
+  const int nh = a.Hkv * a.B;
+  int kb, hh;
+  if (nh % 8 == 0) {
+    const int per = nh / 8, k = blockIdx.x / 8;
+    kb = k / per;
+    hh = (blockIdx.x % 8) * per + k % per;
+  } else {
+    const int id = xcd_remap(blockIdx.x, nkb * nh);
+    kb = id % nkb;
+    hh = id / nkb;
+  }
+  const int kvh = hh % a.Hkv;
+  const int b = hh / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g16 = lane >> 4;
+  const int col = lane & 31, half = lane >> 5;
   const int k0 = kb * kKvKeys;
   const int kw0 = k0 + wave * kKvWaveKeys;
-  const int key = kw0 + (lane & 15);
+  const int key = kw0 + col;
   const int off_q = a.Lk - a.Lq;
   const size_t k_row0 = (size_t)(b * a.Hkv + kvh) * a.Lk;
 
-  // K^T / V^T B operands of the wave's 16 keys: key l%16, d = 32ks + 8*(l/16) ..
-  bf16x8 kf[D / 32], vf[D / 32];
+  copy_v_block<D>(a.v + k_row0 * D, k0, a.Lk, VB, wave, lane);
+  // K^T B operand of the wave's 32 keys: key col, d = 16 ks + 8 half ..
+  bf16x8 kf[D / 16];
   {
     const int kr = min(key, a.Lk - 1);
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      kf[ks] = as_bf16x8(*(const u32x4*)(a.k + (k_row0 + kr) * D + ks * 32 + g16 * 8));
-      vf[ks] = as_bf16x8(*(const u32x4*)(a.v + (k_row0 + kr) * D + ks * 32 + g16 * 8));
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      kf[ks] = as_bf16x8(*(const u32x4*)(a.k + (k_row0 + kr) * D + ks * 16 + half * 8));
   }
-  f32x4 dk[D / 16], dv[D / 16];
+  f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) dk[db] = dv[db] = (f32x4){};
+  for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = (f32x16){};
 
-  // query rows that can see a key of [k0, k0 + 64): positions p in
-  // [k0, k0 + 63 + window - 1] (or [k0, Lk) without a window)
+  // query rows that can see a key of [k0, k0 + 128): positions p in
+  // [k0, k0 + 127 + window - 1] (or [k0, Lk) without a window)
   const int i_lo = max(0, k0 - off_q);
   const int i_hi = min(a.Lq, (a.window > 0 ? k0 + kKvKeys - 1 + a.window : a.Lk) - off_q);
   const int t_begin = i_lo / kKvRows;
   const int nt = i_hi > i_lo ? (i_hi + kKvRows - 1) / kKvRows - t_begin : 0;
   const int steps = G * nt;
 
-  // per-lane LDS read addresses: Q/dO rows of block b in the order
-  // m -> 8(m/4) + 4b + m%4, chunk 4ks + g16; transposed reads: rows 8g16 +
-  // (l%16)/4 (+4), d = 16db + 4((l%16)%4)
+  // per-lane LDS read addresses: Q/dO rows (and V rows) key_perm(col), chunk
+  // 2 ks + half; transposed reads: rows 8 half + (l%16)/4 (+4), d = 32 db +
+  // 16 ((l/16)%2) + 4 (l%4), as for V^T in the forward
   using T = BfTile<D>;
-  int qa[2][D / 32], ta[2][D / 16];
+  int qa[D / 16], ta[2][D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qa[ks] = T::off(key_perm(col), (ks * 2 + half) * 16);
   {
-    const int m = lane & 15;
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        qa[bb][ks] = T::off(8 * (m >> 2) + 4 * bb + (m & 3), (4 * ks + g16) * 16);
+    const int trow = half * 8 + ((lane & 15) >> 2);
+    const int tbyte = (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        ta[e][db] = T::off(8 * g16 + (m >> 2) + 4 * e, 2 * (16 * db + 4 * (m & 3)));
+      for (int db = 0; db < D / 32; ++db) ta[e][db] = T::off(trow + 4 * e, db * 64 + tbyte);
   }
+  const int vw_off = wave * kKvWaveKeys * D * 2;
 
   RowTileCopy<D> cp;
   cp.init(wave, lane);
@@ -518,6 +559,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     tile_rows(0, row0, r0);
     cp.issue(a, row0, min(kKvRows, a.Lq - r0), Q0, G0, S0);
   }
+  const float inv_scale = 1.0f / a.scale;
   auto step = [&](int n, const lds_char* qs, const lds_char* gs, const lds_char* ss, lds_char* qn,
                   lds_char* gn, lds_char* sn) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -529,7 +571,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       cp.issue(a, row0, min(kKvRows, a.Lq - r0), qn, gn, sn);
     }
     const int r0 = (t_begin + n % nt) * kKvRows;
-    // rows [r0, r0+32) against the wave's keys [kw0, kw0+16)
+    // rows [r0, r0+32) against the wave's keys [kw0, kw0+32)
     const int p_first = r0 + off_q, p_last = min(r0 + kKvRows, a.Lq) - 1 + off_q;
     int kind = 2;
     if (kw0 > p_last || kw0 >= a.Lk || (a.window > 0 && kw0 + kKvWaveKeys - 1 <= p_first - a.window))
@@ -537,25 +579,44 @@ void bwd_dkdv_kernel(BwdArgs a) {
     else if (r0 + kKvRows <= a.Lq && kw0 + kKvWaveKeys <= a.Lk && kw0 + kKvWaveKeys - 1 <= p_first &&
              (a.window <= 0 || kw0 > p_last - a.window))
       kind = 1;
-    if (kind != 0)
-      dkdv_tile<D>(qs, gs, ss, qa, ta, kf, vf, dk, dv, kind, r0, key, off_q, a.Lq, a.Lk, a.window,
-                   g16, a.c);
+    if (kind != 0) {
+      // offsets o = row - (r0 + 8 half) of the lane's visible rows: o >= key -
+      // off_q - r0 - 8 half (causal), o < that + window, o < Lq - r0 - 8 half;
+      // none if key >= Lk
+      const int o_lo = key - off_q - r0 - 8 * half;
+      int o_hi = a.Lq - r0 - 8 * half - 1;
+      if (a.window > 0) o_hi = min(o_hi, o_lo + a.window - 1);
+      const unsigned span = (key < a.Lk && o_hi >= o_lo) ? (unsigned)(o_hi - o_lo) : 0u;
+      const int lo = (key < a.Lk && o_hi >= o_lo) ? o_lo : (1 << 30);
+      // the V block's per-wave base is re-derived every step so that the
+      // compiler adds it per read instead of holding 8 summed addresses
+      int vo = vw_off;
+      asm volatile("" : "+s"(vo));
+      dkdv_tile<D>(qs, gs, ss, VB + vo, qa, ta, kf, dk, dv, kind, lo, span, half, a.c, inv_scale);
+    }
   };
   for (int n = 0; n < steps; n += 2) {
     step(n, Q0, G0, S0, Q1, G1, S1);
     if (n + 1 >= steps) break;
     step(n + 1, Q1, G1, S1, Q0, G0, S0);
   }
+  // a work-group with no rows never waited for its V block
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   if (key >= a.Lk) return;
+  // accumulator register 4j + e of block db: d = 32 db + 8 j + 4 half + e
   float* dkp = a.dk + (k_row0 + key) * D;
   float* dvp = a.dv + (k_row0 + key) * D;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    const int d = 16 * db + 4 * g16;
-    *(f32x4*)(dkp + d) = dk[db] * a.scale;
-    *(f32x4*)(dvp + d) = dv[db];
-  }
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * db + 8 * j + 4 * half;
+      const f32x4 xk = {dk[db][4 * j], dk[db][4 * j + 1], dk[db][4 * j + 2], dk[db][4 * j + 3]};
+      const f32x4 xv = {dv[db][4 * j], dv[db][4 * j + 1], dv[db][4 * j + 2], dv[db][4 * j + 3]};
+      *(f32x4*)(dkp + d) = xk * a.scale;
+      *(f32x4*)(dvp + d) = xv;
+    }
 }
 
 }  // namespace
@@ -576,27 +637,19 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* 
   const int rows = kBfWaves / HG * kRowsPerWave;
   a.n_qtiles = (Lq + rows - 1) / rows;
 
-  const long long nrows = (long long)B * Hq * Lq;
-  const int pre_grid = (int)min((nrows + 16 * kDeltaRows - 1) / (16 * kDeltaRows), 65536LL);
-  if (D == 128) {
-    if (o_f32) hipLaunchKernelGGL((bwd_delta_kernel<128, true>), dim3(pre_grid), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_delta_kernel<128, false>), dim3(pre_grid), dim3(256), 0, stream, a);
-  } else {
-    if (o_f32) hipLaunchKernelGGL((bwd_delta_kernel<64, true>), dim3(pre_grid), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_delta_kernel<64, false>), dim3(pre_grid), dim3(256), 0, stream, a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int dq_grid = a.n_qtiles * (Hq / HG) * B;
   const int kv_grid = (Lk + kKvKeys - 1) / kKvKeys * Hkv * B;
   if (D == 128) {
+    if (o_f32) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), dim3(dq_grid), dim3(kBfThreads), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), dim3(dq_grid), dim3(kBfThreads), 0, stream, a);
     hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(kv_grid), dim3(kBfThreads), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(dq_grid), dim3(kBfThreads), 0, stream, a);
   } else {
+    if (o_f32) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), dim3(dq_grid), dim3(kBfThreads), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<64, false>), dim3(dq_grid), dim3(kBfThreads), 0, stream, a);
     hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(kv_grid), dim3(kBfThreads), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(dq_grid), dim3(kBfThreads), 0, stream, a);
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // dsink from the D_i that the dQ kernel rewrote
   if (dsink && sinks)
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3(Hq), dim3(kSinkThreads), 0, stream, a);

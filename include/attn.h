@@ -137,11 +137,11 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
  * With P_ij = exp(s_ij - LSE_i), Psink_i = exp(sink - LSE_i) (LSE of attn_fwd,
  * the sink included) and D_i = <dO_i, O_i>:  dV = P^T dO,  dS = P (dO V^T - D),
  * dQ = scale dS K,  dK = scale dS^T Q,  dsink_h = -sum_{b,i} Psink_i D_i.
- * The flash-attention profile's backward: a dK/dV phase and a dQ phase.  Its
- * issue #2969 is that dsink loses precision when D comes from a bf16-rounded
- * O; here dsink uses D_i = sum_j P_ij (dO_i . v_j) summed in fp32 inside the
- * dQ phase, which does not depend on O at all.  O (bf16 or fp32) only feeds
- * the D of dS.
+ * The flash-attention profile's backward: a dQ phase (rows fixed), then a
+ * dK/dV phase (keys fixed).  Its issue #2969 is that dsink loses precision
+ * when D comes from a bf16-rounded O; here the dQ phase sums D_i = sum_j P_ij
+ * (dO_i . v_j) in fp32, which does not depend on O at all, and dK, dV and
+ * dsink use that.  O (bf16 or fp32) only feeds the D of the dQ phase's dS.
  *
  * q, dout [B,Hq,Lq,D] bf16; k, v [B,Hkv,Lk,D] bf16 (in_dtype must be ATTN_BF16)
  * out  [B,Hq,Lq,D] out_dtype: the O that attn_fwd returned for these inputs

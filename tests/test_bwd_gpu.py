@@ -71,15 +71,16 @@ def oracle_bwd(q, k, v, sinks, dout, window, scale):
                                 window, scale)
 
 
+@pytest.mark.parametrize("o_f32", [True, False])
 @pytest.mark.parametrize("name,L", [("swa_prefill", 700), ("causal_prefill", 400),
                                     ("long_swa_prefill", 900)])
-def test_bwd_workload_reduced(gpu, name, L):
+def test_bwd_workload_reduced(gpu, name, L, o_f32):
     w = W.WORKLOADS[name]
     q, k, v, s = W.prefill_inputs(w, L=L)
     rng = np.random.default_rng(L)
     dout = W.f32_to_bf16_bits(rng.standard_normal(q.shape, dtype=np.float32))
-    say(f"bwd {name} L={L}")
-    got = run_bwd(q, k, v, s, dout, w.window, w.scale)
+    say(f"bwd {name} L={L} O {'fp32' if o_f32 else 'bf16'}")
+    got = run_bwd(q, k, v, s, dout, w.window, w.scale, o_f32=o_f32)
     check_bwd(got, oracle_bwd(q, k, v, s, dout, w.window, w.scale), f"{name} L={L}")
 
 
@@ -130,17 +131,19 @@ def test_bwd_dsink_does_not_depend_on_o(gpu):
 
 
 @pytest.mark.timeout(900)
-def test_bwd_full_size_swa_sampled(gpu):
+@pytest.mark.parametrize("o_f32", [False, True])
+def test_bwd_full_size_swa_sampled(gpu, o_f32):
     """Full sliding-window workload: dK/dV of sampled 64-key blocks (every row
     that sees them, all heads of the KV head) and dQ of those rows, against the
-    oracle on the slice of rows and keys that decides them exactly."""
+    oracle on the slice of rows and keys that decides them exactly.  bf16 O is
+    the launch the benchmark times."""
     w = W.SWA_PREFILL
     say("bwd full size: inputs")
     q, k, v, s = W.prefill_inputs(w)
     rng = np.random.default_rng(17)
     dout = W.f32_to_bf16_bits(rng.standard_normal(q.shape, dtype=np.float32))
     say("bwd full size: running")
-    dq, dk, dv, ds = run_bwd(q, k, v, s, dout, w.window, w.scale)
+    dq, dk, dv, ds = run_bwd(q, k, v, s, dout, w.window, w.scale, o_f32=o_f32)
     G = w.Hq // w.Hkv
     for kvh, k0 in ((0, 0), (3, 4032), (7, w.L - 64)):
         r_a, r_b = k0, min(w.L, k0 + 64 + w.window - 1)
