@@ -120,20 +120,32 @@ __device__ __forceinline__ void dq_tile(const lds_char* ks_, const lds_char* vs_
     pt0 = mfma_32x32x16(v0, df[ks], pt0);
     pt1 = mfma_32x32x16(v1, df[ks], pt1);
   }
+  float sv[32];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    sv[v] = st0[v];
+    sv[16 + v] = st1[v];
+  }
+  // Masked keys get score -inf (P = 0), in one block that only boundary
+  // tiles run (a per-element select would run on every tile).
+  if (kind == 2) {
+    const unsigned lo = (unsigned)(vis_lo - t0);
+    const unsigned span = (unsigned)(vis_hi - vis_lo);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const unsigned j = (unsigned)(kb * 32 + key_of_reg(v, half));
+        sv[kb * 16 + v] = (j - lo <= span) ? sv[kb * 16 + v] : kNegInf;
+      }
+  }
   float ds[32];
-  const unsigned lo = (unsigned)(vis_lo - t0);
-  const unsigned span = (unsigned)(vis_hi - vis_lo);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float s = kb ? st1[v] : st0[v];
       const float dp = kb ? pt1[v] : pt0[v];
-      float p = exp2_fast(__builtin_fmaf(s, c, -lse2));
-      if (kind == 2) {
-        const unsigned j = (unsigned)(kb * 32 + key_of_reg(v, half));
-        p = (j - lo <= span) ? p : 0.0f;
-      }
+      const float p = exp2_fast(__builtin_fmaf(sv[kb * 16 + v], c, -lse2));
       ds[kb * 16 + v] = p * (dp - dl);
       dsum = __builtin_fmaf(p, dp, dsum);
     }
@@ -436,13 +448,18 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs
     dp = mfma_32x32x16(as_bf16x8(lds_read16(gs, qa[ks])), as_bf16x8(lds_read16(vw, qa[ks])), dp);
   }
   // register v sits at row offset key_of_reg(v, 0) from the lane's first row
-  // (row_base + 8 half); it is visible iff that offset lies in
-  // [vis_lo, vis_lo + vis_span]
+  // (row_base + 8 half); it is visible iff that offset lies in [vis_lo,
+  // vis_lo + vis_span].  Masked pairs get -inf (P = 0) in one block that only
+  // boundary steps run.
+  if (kind == 2) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      s[v] = ((unsigned)(key_of_reg(v, 0) - vis_lo) <= vis_span) ? s[v] : kNegInf;
+  }
   float pv[16], dsv[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    float p = exp2_fast(s[v] * c);
-    if (kind == 2) p = ((unsigned)(key_of_reg(v, 0) - vis_lo) <= vis_span) ? p : 0.0f;
+    const float p = exp2_fast(s[v] * c);
     pv[v] = p;
     dsv[v] = p * dp[v];
   }
