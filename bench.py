@@ -50,17 +50,30 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources' code (comments ignored), plus the compile flags;
-    stored traffic counters are used only while it matches."""
+# The sources each profiled kernel is built from (its own file and the headers
+# it includes); a change elsewhere leaves its stored counters valid.
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ("attn_fwd.hip", "attn_common.hpp", "attn_tiles.hpp", "attn_kernels.hpp"),
+    "decode_kernel": ("attn_decode.hip", "attn_common.hpp", "attn_kernels.hpp"),
+    "combine_kernel": ("attn_decode.hip", "attn_common.hpp", "attn_kernels.hpp"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code (comments ignored) of the sources that build `kernel`
+    (a name of KERNEL_SOURCES, template arguments and workload allowed after
+    it), plus their compile flags; stored counters are used only while it
+    matches."""
     from exact_attention_attn_amd import build as B
+    base = kernel.split("<")[0].split(":")[0]
+    files = KERNEL_SOURCES[base]
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_attn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), encoding="utf-8") as f:
-                h.update(name.encode() + _code_only(f.read()).encode())
-    h.update(repr((B.DEVICE_FLAGS, sorted(B.SOURCE_FLAGS.items()))).encode())
+    for name in files:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
+    flags = [B.SOURCE_FLAGS.get(n, []) for n in files]
+    h.update(repr((B.DEVICE_FLAGS, flags)).encode())
     return h.hexdigest()[:16]
 
 
@@ -73,7 +86,7 @@ def stored_profile(kernel: str) -> dict:
     with open(path) as f:
         data = json.load(f)
     ent = data.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return {}
     return ent
 
