@@ -209,8 +209,8 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
 
 
 def measure_backward(A, torch, dev, stream, q, k, v, s, wp, reps=10):
-    """attn_bwd on the step's prefill: dQ, dK, dV and dsink for a seeded dO,
-    given the bf16 O that the forward writes in the step.
+    """attn_bwd on a prefill workload's inputs: dQ, dK, dV and dsink for a
+    seeded dO, given the bf16 O that the forward writes in the step.
 
     Algorithmic work is the five products of the backward (S, dP, dV, dK, dQ:
     10*D flops per unmasked pair, 2.5x the forward); the two phases both
@@ -232,8 +232,10 @@ def measure_backward(A, torch, dev, stream, q, k, v, s, wp, reps=10):
                              scale=wp.scale, stream=stream)
     t = warm_then_time(torch, stream, run, reps)
     pairs = wp.flops() // (4 * wp.D)
-    return {"entry": "attn_bwd (dQ, dK, dV, dsink), bf16 O", "ms": round(t * 1e3, 4),
+    return {"entry": "attn_bwd (dQ, dK, dV, dsink), bf16 O", "workload": wp.name,
+            "ms": round(t * 1e3, 4),
             "TFLOP/s": round(10 * wp.D * pairs / t / 1e12, 2),
+            "frac": round(10 * wp.D * pairs / t / 1e12 / PEAK_BF16_TFLOPS, 4),
             "executed_TFLOP/s": round(14 * wp.D * pairs / t / 1e12, 2),
             "note": "TFLOP/s counts the 5 backward products (10*D per pair); both phases "
                     "compute S and dP (14*D per pair executed)"}
@@ -678,6 +680,9 @@ def main():
             A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
             t_dec.mean() + t_cmb.mean(), wl)
         extras["backward"] = measure_backward(A, torch, dev, stream, ql, kl, vl, sk, wl)
+        if "causal_prefill" in leg_inputs:
+            wc, qc, kc, vc, sc = leg_inputs["causal_prefill"]
+            extras["backward_causal"] = measure_backward(A, torch, dev, stream, qc, kc, vc, sc, wc)
         ol = torch.empty(ql.shape, dtype=torch.bfloat16, device=dev)
         ll = torch.empty(ql.shape[:3], dtype=torch.float32, device=dev)
         ml_row = torch.empty(ll.shape, dtype=torch.float32, device=dev)
