@@ -120,6 +120,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* ks_, const lds_char* vs_
     pt0 = mfma_32x32x16(v0, df[ks], pt0);
     pt1 = mfma_32x32x16(v1, df[ks], pt1);
   }
+  __builtin_amdgcn_s_setprio(3);  // VALU phase: see the forward's softmax
   float sv[32];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -157,6 +158,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* ks_, const lds_char* vs_
       const float* x = ds + kb * 16 + s2 * 8;
       pf[kb][s2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int i = 0; i < 4 * NDB; ++i) {
     const int db = i % NDB, ks2 = i / NDB;
@@ -451,6 +453,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs
   // (row_base + 8 half); it is visible iff that offset lies in [vis_lo,
   // vis_lo + vis_span].  Masked pairs get -inf (P = 0) in one block that only
   // boundary steps run.
+  __builtin_amdgcn_s_setprio(3);  // VALU phase: see the forward's softmax
   if (kind == 2) {
 #pragma unroll
     for (int v = 0; v < 16; ++v)
@@ -471,6 +474,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs
     pp[k2] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     pd[k2] = pack_bf16x8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
   }
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll

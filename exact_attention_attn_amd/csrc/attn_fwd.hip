@@ -272,6 +272,9 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
 #pragma unroll
   for (int i = 0; i < VA; ++i) vread(i);
 
+  // The softmax below runs at raised wave priority: while this wave has VALU
+  // work, the SIMD's other wave (in its MFMA phase) issues only between it.
+  __builtin_amdgcn_s_setprio(3);
   float s[32];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -309,6 +312,7 @@ __device__ __forceinline__ void bf16_tile(const lds_char* ks_, const lds_char* v
     }
   row.lb = sum_bf16_words(pw[1][0], pw[1][1], sum_bf16_words(pw[0][0], pw[0][1], row.lb));
 
+  __builtin_amdgcn_s_setprio(0);
   // O^T += V^T P^T: step (kb, s2) feeds the D/32 independent accumulators.
 #pragma unroll
   for (int i = 0; i < NSTEP; ++i) {
