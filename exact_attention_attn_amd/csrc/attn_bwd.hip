@@ -26,7 +26,6 @@
 #include "attn_kernels.hpp"
 #include "attn_tiles.hpp"
 
-#include <type_traits>
 
 namespace attn {
 
