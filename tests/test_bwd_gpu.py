@@ -156,3 +156,37 @@ def test_bwd_full_size_swa_sampled(gpu, o_f32):
         got = (dq[:, heads, r_a:r_b], dk[:, kvh:kvh + 1, k0:k0 + 64], dv[:, kvh:kvh + 1, k0:k0 + 64], None)
         ref = (want[0], want[1][:, :, k0 - c_a:k0 - c_a + 64], want[2][:, :, k0 - c_a:k0 - c_a + 64], None)
         check_bwd(got, ref, f"full swa kvh={kvh} keys {k0}..{k0 + 63}")
+
+
+@pytest.mark.timeout(900)
+def test_bwd_full_size_causal_sampled(gpu):
+    """Full causal workload (B4 Hq32 Hkv8 L4096), bf16 O as the benchmark's
+    causal backward launches it: dK/dV of two 64-key blocks of one (batch, KV
+    head), every row that sees them being rows k0 .. L-1 of the group's heads,
+    and dQ of those rows, against the oracle on rows [k0, L) and keys [0, L)
+    (which decide them exactly under the causal mask); and dQ of rows 0..63,
+    which see only keys 0..63."""
+    w = W.CAUSAL_PREFILL
+    say("bwd full size causal: inputs")
+    q, k, v, s = W.prefill_inputs(w)
+    rng = np.random.default_rng(23)
+    dout = W.f32_to_bf16_bits(rng.standard_normal(q.shape, dtype=np.float32))
+    say("bwd full size causal: running")
+    dq, dk, dv, _ = run_bwd(q, k, v, s, dout, w.window, w.scale, o_f32=False)
+    G = w.Hq // w.Hkv
+    b, kvh = 1, 5
+    heads = slice(kvh * G, (kvh + 1) * G)
+    sub = lambda x, h, a, c: host_values(x[b:b + 1, h, a:c], W.BF16)
+    for k0 in (w.L - 64, 1984):
+        want = oracle.attention_bwd(sub(q, heads, k0, w.L), sub(k, slice(kvh, kvh + 1), 0, w.L),
+                                    sub(v, slice(kvh, kvh + 1), 0, w.L), s[heads],
+                                    sub(dout, heads, k0, w.L), w.window, w.scale)
+        got = (dq[b:b + 1, heads, k0:], dk[b:b + 1, kvh:kvh + 1, k0:k0 + 64],
+               dv[b:b + 1, kvh:kvh + 1, k0:k0 + 64], None)
+        ref = (want[0], want[1][:, :, k0:k0 + 64], want[2][:, :, k0:k0 + 64], None)
+        check_bwd(got, ref, f"full causal b={b} kvh={kvh} keys {k0}..{k0 + 63}")
+    want = oracle.attention_bwd(sub(q, heads, 0, 64), sub(k, slice(kvh, kvh + 1), 0, 64),
+                                sub(v, slice(kvh, kvh + 1), 0, 64), s[heads],
+                                sub(dout, heads, 0, 64), w.window, w.scale)
+    d = np.abs(dq[b:b + 1, heads, :64] - want[0])
+    assert d.max() <= TOL_MAX * np.abs(want[0]).max(), f"full causal dq rows 0..63: {d.max():.3e}"
