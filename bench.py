@@ -145,8 +145,20 @@ def warm_then_time(torch, stream, fn, reps, warm_s=0.04):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
+def time_calls(torch, stream, fn, reps):
+    """Seconds per call of fn over reps back-to-back calls on stream (events)."""
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
 def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd,
-                           seqlens, reps=20):
+                           seqlens, reps=10, rounds=7):
     """GB/s of decode + combine under several split-count policies.
 
     Rows: the decode workload of the step, and two synthetic mixes drawn on
@@ -155,8 +167,11 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
     caller plans once per step and can reuse the plan while its lengths
     stand); 'auto+plan' also times the planning launch (attn_decode_plan)
     inside every call.  auto_vs_best_fixed = auto / the fastest fixed rule.
+    Each policy is timed in `rounds` interleaved rounds of `reps` calls.
     """
-    def timed(q_, k_, v_, sl_, Lk_max, policy, param, nbytes, with_plan=False):
+    def setup(q_, k_, v_, sl_, Lk_max, policy, param, with_plan=False):
+        """The policy's planned counts and one decode + combine call (plus the
+        planning launch when with_plan)."""
         B, Hq = q_.shape[0], q_.shape[1]
         ns = torch.empty(B, dtype=torch.int32, device=dev)
         plan = lambda: A.attn_decode_plan(sl_, ns, Hq=Hq, Hkv=k_.shape[1], Lk_max=Lk_max,
@@ -178,11 +193,8 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
                            stream=stream)
         with torch.cuda.stream(stream):
             plan()
-        ms = warm_then_time(torch, stream, once, reps) * 1e3
         label = f"{policy}({param})" if policy != "auto" else ("auto+plan" if with_plan else "auto")
-        return {"policy": label,
-                "us": round(ms * 1e3, 1), "GB/s": round(nbytes / ms / 1e6, 1),
-                "total_splits": int(ns.sum().item())}
+        return label, ns, once
 
     rows = []
     Hq, Hkv, D = wd.Hq, wd.Hkv, wd.D
@@ -198,9 +210,23 @@ def measure_split_policies(A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, do
         mixes.append((name, q_, k_, v_, torch.from_numpy(lens.astype(np.int32)).to(dev), Lk_max, lens))
     for name, q_, k_, v_, sl_, Lk_max, lens in mixes:
         nbytes = decode_bytes(lens, Hq, Hkv, D, 0)
-        res = [timed(q_, k_, v_, sl_, Lk_max, pol, par, nbytes)
-               for pol, par in (("auto", 0), ("keys", 1024), ("keys", 512), ("count", 1))]
-        res.append(timed(q_, k_, v_, sl_, Lk_max, "auto", 0, nbytes, with_plan=True))
+        cases = [setup(q_, k_, v_, sl_, Lk_max, pol, par)
+                 for pol, par in (("auto", 0), ("keys", 1024), ("keys", 512), ("count", 1))]
+        cases.append(setup(q_, k_, v_, sl_, Lk_max, "auto", 0, with_plan=True))
+        # The policies alternate within each round (the starting one rotates), so a
+        # slow drift of the clock touches all of them alike; the median per policy
+        # over the rounds is reported.
+        warm_then_time(torch, stream, lambda: [c[2]() for c in cases], 1)
+        per = [[] for _ in cases]
+        for r in range(rounds):
+            for j in range(len(cases)):
+                i = (j + r) % len(cases)
+                per[i].append(time_calls(torch, stream, cases[i][2], reps))
+        res = []
+        for (label, ns, _), ts in zip(cases, per):
+            ms = float(np.median(ts)) * 1e3
+            res.append({"policy": label, "us": round(ms * 1e3, 1),
+                        "GB/s": round(nbytes / ms / 1e6, 1), "total_splits": int(ns.sum().item())})
         best_fixed = min(r["us"] for r in res if not r["policy"].startswith("auto"))
         rows.append({"workload": name, "results": res,
                      "auto_vs_best_fixed": round(res[0]["us"] / best_fixed, 4),
