@@ -317,8 +317,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 //                 row order the k order of these B operands)
 // The S accumulator starts at -LSE/scale and the dP accumulator at -D, so the
 // MFMAs deliver c S - LSE log2e (after one multiply by c) and dP - D directly.
-// Each K^T/V^T operand byte read feeds a 32x32x16 MFMA: half the LDS bytes per
-// flop of 16-key blocks on 16x16x32 MFMAs.  V sits in LDS (not in VGPRs) so
+// Every LDS operand read (16 B per lane) feeds a 32x32x16 MFMA: half the LDS
+// bytes per flop of 16-key blocks on 16x16x32 MFMAs.  V sits in LDS (not in VGPRs) so
 // that K^T, the dK^T/dV^T accumulators and two 32x32 tiles fit in the 256
 // registers of two waves per SIMD; its rows are stored in key_perm order
 // within each wave's 32 keys, so a V^T operand read has the address of the
@@ -486,7 +486,8 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs
     }
 }
 
-// At most two waves per SIMD (the registers allow no more).
+// Two waves per SIMD: D = 128 takes about 240 of their 256 registers each
+// (D = 64 is held to the same occupancy).
 template <int D>
 __global__ __launch_bounds__(kBfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
