@@ -143,3 +143,15 @@ def run_decode_repeated(q, kc, vc, seqlens, nsplits, sinks, window, scale, repea
                     lse.cpu().numpy()))
     del qd, kd, vd, op, lp, out, lse
     return res
+
+
+_FULL_DECODE = {}
+
+
+def full_decode_inputs():
+    """The split-KV decode workload at full size (host arrays, generated once per
+    test session and shared by the test modules that use it)."""
+    if not _FULL_DECODE:
+        say("splitkv_decode full size: generating inputs")
+        _FULL_DECODE["x"] = W.decode_inputs(W.SPLITKV_DECODE)
+    return _FULL_DECODE["x"]

@@ -14,7 +14,7 @@ import oracle
 from exact_attention_attn_amd import workloads as W
 
 gpu_util = pytest.importorskip("gpu_util")
-from gpu_util import (compare, host_values, run_decode, run_decode_repeated,  # noqa: E402
+from gpu_util import (full_decode_inputs, compare, host_values, run_decode, run_decode_repeated,  # noqa: E402
                       run_fwd, say)
 
 pytestmark = pytest.mark.gpu
@@ -343,17 +343,6 @@ def test_decode_matches_forward_with_one_query(gpu):
         of, lf = run_fwd(q, k, v, sinks, W.BF16, window, D ** -0.5)
         compare(o, l, of[:, :, 0].astype(np.float64), lf[:, :, 0].astype(np.float64),
                 f"decode vs fwd W={window}", tol_max=2e-3, tol_mean=2e-4, tol_lse=2e-4)
-
-
-_FULL_DECODE = {}
-
-
-def full_decode_inputs():
-    """The split-KV decode workload at full size (generated once per session)."""
-    if not _FULL_DECODE:
-        say("splitkv_decode full size: generating inputs")
-        _FULL_DECODE["x"] = W.decode_inputs(W.SPLITKV_DECODE)
-    return _FULL_DECODE["x"]
 
 
 @pytest.mark.timeout(900)

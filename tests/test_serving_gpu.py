@@ -14,7 +14,7 @@ import oracle
 from exact_attention_attn_amd import workloads as W
 
 gpu_util = pytest.importorskip("gpu_util")
-from gpu_util import compare, host_values, run_decode, say, to_dev  # noqa: E402
+from gpu_util import compare, full_decode_inputs, host_values, run_decode, say, to_dev  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -166,3 +166,65 @@ def test_varlen_prefill(gpu, case, D, Hq, Hkv, window):
         d_o = np.abs(out[0].cpu().numpy() - o[:, cu_q[b]:cu_q[b + 1]]).max()
         d_l = np.abs(lse[0].cpu().numpy() - l[:, cu_q[b]:cu_q[b + 1]]).max()
         assert d_o <= 1e-5 and d_l <= 1e-5, f"b={b}: varlen vs dense {d_o:.3e} {d_l:.3e}"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("page_size", [16, 256])
+def test_paged_decode_full_size(gpu, page_size):
+    """The benchmark's serving layout: the full split-KV decode cache (B64 Hq64
+    Hkv8 D128, 1.0M cached keys) in shuffled pages of 16 or 256 keys, built on
+    the device; paged decode + combine against the dense decode + combine on
+    the same splits (the dense path is checked against the oracle at this
+    size elsewhere), and two sequences against the oracle directly."""
+    w = W.SPLITKV_DECODE
+    q, kc, vc, seqlens, ns, s = full_decode_inputs()
+    B, Hkv, Lk_max, D = kc.shape
+    P = page_size
+    mp = Lk_max // P
+    need = [-(-int(L) // P) for L in seqlens]
+    total = sum(need)
+    perm = np.random.default_rng(P).permutation(total)
+    table = np.full((B, mp), 1 << 30, dtype=np.int32)  # unused slots: never read
+    src = np.empty(total, dtype=np.int64)
+    i = 0
+    for b in range(B):
+        for p in range(need[b]):
+            table[b, p] = perm[i]
+            src[perm[i]] = b * mp + p
+            i += 1
+    say(f"paged decode full size, {P}-key pages: building {total} pages")
+    qd = to_dev(q, W.BF16)
+    sl = torch.from_numpy(np.asarray(seqlens, np.int32)).cuda()
+    nsd = torch.from_numpy(np.asarray(ns, np.int32)).cuda()
+    sd = torch.from_numpy(np.asarray(s, np.float32)).cuda()
+    bt = torch.from_numpy(table).cuda()
+    idx = torch.from_numpy(src).cuda()
+    outs = {}
+    for layout in ("dense", "paged"):
+        kd, vd = to_dev(kc, W.BF16), to_dev(vc, W.BF16)
+        if layout == "paged":
+            page = lambda x: x.view(B, Hkv, mp, P, D).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, D)[idx].contiguous()
+            kd, vd = page(kd), page(vd)
+        op = torch.full((B, w.Hq, 64, D), float("nan"), device="cuda")
+        lp = torch.full((B, w.Hq, 64), float("nan"), device="cuda")
+        out = torch.empty((B, w.Hq, 1, D), device="cuda")
+        lse = torch.empty((B, w.Hq), device="cuda")
+        if layout == "paged":
+            A.attn_decode_splitkv_paged(qd, kd, vd, bt, sl, nsd, op, lp, window=0, scale=w.scale)
+        else:
+            A.attn_decode_splitkv(qd, kd, vd, sl, nsd, op, lp, window=0, scale=w.scale)
+        A.attn_combine(op, lp, sl, nsd, sd, out, lse, Lk_max=Lk_max, window=0)
+        torch.cuda.synchronize()
+        outs[layout] = (out[:, :, 0].cpu().numpy(), lse.cpu().numpy(), np.isnan(op.cpu().numpy()))
+        del kd, vd, op, lp, out, lse
+        torch.cuda.empty_cache()
+    o, l, nan_p = outs["paged"]
+    o_d, l_d, nan_d = outs["dense"]
+    d_o, d_l = np.abs(o - o_d).max(), np.abs(l - l_d).max()
+    say(f"  paged vs dense: max|dO| {d_o:.3e} max|dLSE| {d_l:.3e}")
+    assert d_o <= 1e-5 and d_l <= 1e-5, "paged and dense decode disagree"
+    assert np.array_equal(nan_p, nan_d), "different partial lanes written"
+    picks = [int(np.argmax(seqlens)), 7]
+    o_r, l_r = oracle.decode(host_values(q[picks], W.BF16), host_values(kc[picks], W.BF16),
+                             host_values(vc[picks], W.BF16), seqlens[picks], s, 0, w.scale)
+    compare(o[picks], l[picks], o_r, l_r, f"paged decode full size ps={P}")
