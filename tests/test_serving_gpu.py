@@ -228,3 +228,41 @@ def test_paged_decode_full_size(gpu, page_size):
     o_r, l_r = oracle.decode(host_values(q[picks], W.BF16), host_values(kc[picks], W.BF16),
                              host_values(vc[picks], W.BF16), seqlens[picks], s, 0, w.scale)
     compare(o[picks], l[picks], o_r, l_r, f"paged decode full size ps={P}")
+
+
+@pytest.mark.timeout(900)
+def test_varlen_prefill_bench_size(gpu):
+    """The benchmark's packed batch: 8 sequences of U{1024..8192} rows (the same
+    draw), Hq64 Hkv8 D128, window 513, no sinks, bf16 O.  Every sequence against
+    the dense forward on it alone, and sampled 64-row blocks against the oracle
+    on the slice of keys that decides them."""
+    Hq, Hkv, D, window = 64, 8, 128, 513
+    lens = np.random.default_rng(11).integers(1024, 8193, 8)
+    rng = np.random.default_rng(12)
+    tot = int(lens.sum())
+    bits = lambda shape: W.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    q, k, v = bits((Hq, tot, D)), bits((Hkv, tot, D)), bits((Hkv, tot, D))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    scale = D ** -0.5
+    say(f"varlen bench size: {tot} rows")
+    o, l = run_varlen(q, k, v, cu, cu, None, window, scale, int(lens.max()), out_f32=False)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    for b in range(len(lens)):
+        a, e = int(cu[b]), int(cu[b + 1])
+        qd = to_dev(q[None, :, a:e], W.BF16)
+        kd, vd = to_dev(k[None, :, a:e], W.BF16), to_dev(v[None, :, a:e], W.BF16)
+        out = torch.empty(qd.shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(qd.shape[:3], device="cuda")
+        A.attn_fwd(qd, kd, vd, None, out, lse, window=window, scale=scale)
+        torch.cuda.synchronize()
+        d_o = np.abs(out[0].float().cpu().numpy() - o[:, a:e]).max()
+        d_l = np.abs(lse[0].cpu().numpy() - l[:, a:e]).max()
+        assert d_o <= 1e-5 and d_l <= 1e-5, f"b={b}: varlen vs dense {d_o:.3e} {d_l:.3e}"
+    for b, h, r0 in ((0, 3, 0), (3, 17, 700), (7, 63, int(lens[7]) - 64)):
+        a = int(cu[b])
+        k0 = max(0, r0 - window + 1)
+        sl = lambda x, hh, lo, hi: host_values(x[None, hh:hh + 1, a + lo:a + hi], W.BF16)
+        o_r, l_r = oracle.attention_fwd(sl(q, h, r0, r0 + 64), sl(k, h // (Hq // Hkv), k0, r0 + 64),
+                                        sl(v, h // (Hq // Hkv), k0, r0 + 64), None, window, scale)
+        compare(o[h, a + r0:a + r0 + 64], l[h, a + r0:a + r0 + 64], o_r[0, 0], l_r[0, 0],
+                f"varlen bench size b={b} h={h} rows {r0}..", bf16_out=True)
