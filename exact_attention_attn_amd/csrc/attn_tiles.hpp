@@ -127,7 +127,7 @@ struct BfSmem {
 
 // Work of one bf16 work-group: the HG query heads hg*HG .. of KV head kvh
 // (they share every K/V tile) over the same rows [r0, r0 + rows).  Longest
-// q-tiles first within each (batch, KV head, head group).
+// q-tiles first within each (batch, KV head).
 struct BfWork {
   int b, kvh, hg, qt;
 };
@@ -148,10 +148,19 @@ __device__ __forceinline__ BfWork decode_bf_work(const Args& a, int n_hg) {
     id = xcd_remap(blockIdx.x, total);
   }
   BfWork w;
-  w.qt = a.n_qtiles - 1 - id % a.n_qtiles;
-  id /= a.n_qtiles;
-  w.hg = id % n_hg;
-  id /= n_hg;
+  if (VARLEN) {
+    w.qt = a.n_qtiles - 1 - id % a.n_qtiles;
+    id /= a.n_qtiles;
+    w.hg = id % n_hg;
+    id /= n_hg;
+  } else {
+    // The head groups of one q-tile are consecutive ids, so they run side by
+    // side on one XCD and each K/V tile comes from HBM once for all of them.
+    w.hg = id % n_hg;
+    id /= n_hg;
+    w.qt = a.n_qtiles - 1 - id % a.n_qtiles;
+    id /= a.n_qtiles;
+  }
   w.kvh = id % a.Hkv;
   w.b = id / a.Hkv;
   return w;
