@@ -83,15 +83,21 @@ def compare(o, l, o_ref, l_ref, what: str, tol_max=TOL_MAX, tol_mean=TOL_MEAN, t
     assert np.isfinite(o).all(), f"{what}: non-finite O"
     d = np.abs(o - o_ref)
     if bf16_out:
-        # rounding O to bf16 adds up to half an ulp of |O|
-        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))) - 7)
-        bound = tol_max + 0.5 * ulp
-        assert (d <= bound).all(), f"{what}: max|dO| {d.max():.3e} beyond bf16 bound"
+        # The bar is for O as accumulated in fp32.  Storing it in bf16 adds its
+        # own rounding, up to half an ulp of |O| per element, to each element
+        # and so to the mean as well: for peaked scores |O| is about |v| and
+        # that rounding alone averages about 1e-3.
+        mag = np.maximum(np.maximum(np.abs(o_ref), np.abs(o)), 1e-30)
+        half_ulp = 0.5 * np.exp2(np.floor(np.log2(mag)) - 7)
+        assert (d <= tol_max + half_ulp).all(), f"{what}: max|dO| {d.max():.3e} beyond bf16 bound"
+        assert d.mean() <= tol_mean + half_ulp.mean(), (
+            f"{what}: mean|dO| = {d.mean():.3e} beyond {tol_mean} + bf16 rounding {half_ulp.mean():.3e}")
     else:
         assert d.max() <= tol_max, f"{what}: max|dO| = {d.max():.3e}"
-    assert d.mean() <= tol_mean, f"{what}: mean|dO| = {d.mean():.3e}"
+        assert d.mean() <= tol_mean, f"{what}: mean|dO| = {d.mean():.3e}"
     both_inf = np.isneginf(l) & np.isneginf(l_ref)
-    dl = np.abs(np.where(both_inf, 0.0, l - l_ref))
+    with np.errstate(invalid="ignore"):  # -inf - -inf where both rows see nothing
+        dl = np.abs(np.where(both_inf, 0.0, l - l_ref))
     assert np.isfinite(dl).all() and dl.max() <= tol_lse, f"{what}: max|dLSE| = {dl.max():.3e}"
     return d.max(), d.mean(), dl.max()
 
