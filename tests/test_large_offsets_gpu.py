@@ -1,4 +1,4 @@
-"""GPU parity beyond 2^32 elements: the largest launches (tensors of 5-17 GB) in
+"""GPU parity beyond 2^32 elements: the largest launches (tensors of 5-17 GB, a paged pool of 2 x 13 GB) in
 which element offsets pass 2^31 and 2^32, checked on sampled rows against the
 float64 oracle.  Inputs are drawn on the device by a seeded torch generator;
 the oracle reads the same values, copied back for the sampled rows' heads.
@@ -151,3 +151,53 @@ def test_backward_offsets_beyond_4g_elements(gpu):
                dv[b:b + 1, kv, k0:k0 + 64].cpu().numpy(), None)
         ref = (want[0], want[1][:, :, k0 - c_a:k0 - c_a + 64], want[2][:, :, k0 - c_a:k0 - c_a + 64], None)
         check_bwd(got, ref, f"large backward b={b} kvh={kvh} keys {k0}..{k0 + 63}")
+
+
+@pytest.mark.timeout(900)
+def test_paged_decode_offsets_beyond_4g_elements(gpu):
+    """Paged split-KV decode over a pool of 16-key pages holding 6.4e9 elements
+    per K and V (B128 Hq64 Hkv8 D128, 32768..65536 keys per sequence, pages
+    shuffled over the pool): sampled sequences, their pages gathered from the
+    pool by the block table, against the oracle."""
+    B, Hq, Hkv, D, P = 128, 64, 8, 128, 16
+    Lmax = 65536
+    scale = D ** -0.5
+    rng = np.random.default_rng(8180)
+    seqlens = rng.integers(32768, Lmax, size=B, endpoint=True).astype(np.int32)
+    need = -(-seqlens // P)
+    total = int(need.sum())
+    perm = rng.permutation(total).astype(np.int32)
+    mp = Lmax // P
+    table = np.full((B, mp), -1, dtype=np.int32)  # unused slots: never read
+    cu = np.concatenate([[0], np.cumsum(need)])
+    for b in range(B):
+        table[b, :need[b]] = perm[cu[b]:cu[b + 1]]
+    nsplits = np.minimum(-(-seqlens // 1024), 64).astype(np.int32)
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8180)
+    say(f"large paged decode: drawing {total} pages on the device")
+    q = _randn(g, (B, Hq, 1, D))
+    kp, vp = _randn(g, (total, Hkv, P, D)), _randn(g, (total, Hkv, P, D))
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.from_numpy(seqlens).cuda()
+    ns = torch.from_numpy(nsplits).cuda()
+    sd = torch.from_numpy(sinks).cuda()
+    op = torch.full((B, Hq, 64, D), float("nan"), device="cuda")
+    lp = torch.full((B, Hq, 64), float("nan"), device="cuda")
+    out = torch.empty((B, Hq, 1, D), device="cuda")
+    lse = torch.empty((B, Hq), device="cuda")
+    say("large paged decode: running")
+    A.attn_decode_splitkv_paged(q, kp, vp, bt, sl, ns, op, lp, window=0, scale=scale)
+    A.attn_combine(op, lp, sl, ns, sd, out, lse, Lk_max=mp * P, window=0)
+    torch.cuda.synchronize()
+    high = int(np.argmax([table[b, :need[b]].max() for b in range(B)]))
+    for b in sorted({0, 77, B - 1, high}):
+        n = int(seqlens[b])
+        say(f"large paged decode: sequence {b} ({n} keys, highest page {int(table[b, :need[b]].max())})")
+        pages = bt[b, :need[b]].long()
+        gather = lambda pool: pool[pages].permute(1, 0, 2, 3).reshape(Hkv, -1, D)[:, :n]
+        o_r, l_r = oracle.decode(_host(q[b:b + 1]), _host(gather(kp))[None], _host(gather(vp))[None],
+                                 seqlens[b:b + 1], sinks, 0, scale)
+        compare(out[b:b + 1, :, 0].cpu().numpy(), lse[b:b + 1].cpu().numpy(), o_r, l_r,
+                f"large paged decode b={b}")
