@@ -19,6 +19,17 @@ from gpu_util import compare, say  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True)
+def _release_device_memory():
+    """Hand the tens of GB these launches reserve back to the device after each
+    test, so that the tests after them start from an empty cache."""
+    yield
+    import gc
+
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def _randn(g, shape):
     return torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
 
