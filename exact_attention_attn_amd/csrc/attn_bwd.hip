@@ -486,7 +486,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qs, const lds_char* gs
     }
 }
 
-// Two waves per SIMD: D = 128 takes about 240 of their 256 registers each
+// Two waves per SIMD: D = 128 takes about 250 of their 256 registers each
 // (D = 64 is held to the same occupancy).
 template <int D>
 __global__ __launch_bounds__(kBfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
