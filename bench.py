@@ -540,10 +540,18 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
+    ap.add_argument("--extras", default="split_policy,serving,backward,max_logit",
+                    help="extras timed after the legs, a comma list of split_policy, serving, "
+                         "backward, max_logit (all by default); the profiled runs of the "
+                         "backward kernels use backward alone")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: attn_fwd and decode rates over a range of shapes, "
                          "one JSON line each")
     args = ap.parse_args()
+    want = set(x for x in args.extras.split(",") if x)
+    unknown = want - {"split_policy", "serving", "backward", "max_logit"}
+    if unknown:
+        ap.error(f"unknown extras: {sorted(unknown)}")
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -700,15 +708,21 @@ def main():
     if not args.step_only and "swa_prefill" in leg_inputs:
         wl, ql, kl, vl, sk = leg_inputs["swa_prefill"]
         say("bench: extras")
-        extras["split_policy"] = measure_split_policies(
-            A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd, seqlens)
-        extras["serving"] = measure_serving(
-            A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
-            t_dec.mean() + t_cmb.mean(), wl)
-        extras["backward"] = measure_backward(A, torch, dev, stream, ql, kl, vl, sk, wl)
-        if "causal_prefill" in leg_inputs:
-            wc, qc, kc, vc, sc = leg_inputs["causal_prefill"]
-            extras["backward_causal"] = measure_backward(A, torch, dev, stream, qc, kc, vc, sc, wc)
+        if "split_policy" in want:
+            extras["split_policy"] = measure_split_policies(
+                A, torch, dev, stream, qd, kd, vd, sl, ds, op, lp, dout, dlse, wd, seqlens)
+        if "serving" in want:
+            extras["serving"] = measure_serving(
+                A, torch, dev, stream, qd, kd, vd, sl, ns, op, lp, dout, dlse, ds, wd, seqlens,
+                t_dec.mean() + t_cmb.mean(), wl)
+        if "backward" in want:
+            extras["backward"] = measure_backward(A, torch, dev, stream, ql, kl, vl, sk, wl)
+            if "causal_prefill" in leg_inputs:
+                wc, qc, kc, vc, sc = leg_inputs["causal_prefill"]
+                extras["backward_causal"] = measure_backward(A, torch, dev, stream, qc, kc, vc,
+                                                             sc, wc)
+    if not args.step_only and "swa_prefill" in leg_inputs and "max_logit" in want:
+        wl, ql, kl, vl, sk = leg_inputs["swa_prefill"]
         ol = torch.empty(ql.shape, dtype=torch.bfloat16, device=dev)
         ll = torch.empty(ql.shape[:3], dtype=torch.float32, device=dev)
         ml_row = torch.empty(ll.shape, dtype=torch.float32, device=dev)
