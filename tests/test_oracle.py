@@ -415,6 +415,33 @@ def test_plan_properties():
     assert oracle.plan_splits([0, -3], 64, 8, 100, 0, 64, "auto", 0, 512) == [1, 1]
 
 
+def test_plan_per_sequence_properties():
+    """Properties any per-sequence plan must have, independent of the rule's
+    constants: the counts follow their sequences under a permutation of the
+    batch, empty sequences change nothing for the others (they add no work)
+    and get one split (a fixed count under "count"), and no sequence gets more splits than it has 256-key
+    chunks (the smallest target) or than max_splits."""
+    rng = np.random.default_rng(31)
+    for trial in range(12):
+        B = int(rng.integers(1, 60))
+        Lk_max = int(rng.choice([2048, 32768, 100000]))
+        window = int(rng.choice([0, 513, 5000]))
+        ms = int(rng.choice([8, 64]))
+        sl = [int(x) for x in rng.integers(0, Lk_max + 10, B)]
+        perm = rng.permutation(B)
+        for policy, param in (("auto", 0), ("keys", 700), ("count", 5)):
+            plan = lambda x: oracle.plan_splits(x, 64, 8, Lk_max, window, ms, policy, param, 256)
+            ns = plan(sl)
+            assert plan([sl[i] for i in perm]) == [ns[i] for i in perm]
+            empty = 1 if policy != "count" else min(param, ms)
+            assert plan(sl + [0, 0, 0]) == ns + [empty] * 3
+            for n, x in zip(ns, sl):
+                v = oa.visible_keys(x, Lk_max, window)
+                assert 1 <= n <= ms
+                if policy == "auto":
+                    assert n <= max(1, -(-v // 256))
+
+
 def test_plan_pins_catch_changed_rule(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(oa, "PLAN_ITEM_COST", 0)
